@@ -1,0 +1,177 @@
+"""Benchmark of the fused ZeRO shard step on one MI355X.
+
+One step = one call of zero_adam_step on the 7.5B-parameter, N_d = 64,
+Stage-2 workload: the owner's 117,187,520-element shard, 64 resident bf16
+gradient slices reduced in rank order in fp32, mixed-precision Adam on the
+fp32 master / m / v, and the fp16 parameters written into the full parameter
+buffer.  Inputs are synthetic (seeded, generated on the GPU) and resident in
+HBM before timing starts.
+
+Prints ONE JSON line on stdout (everything else goes to stderr):
+  value      shard parameters updated per second
+  roofline   algorithmic bytes per launch / average launch time, against
+             MI355X's 8 TB/s HBM peak; traffic from the committed rocprofv3
+             counter summary when it was taken on the current kernel source
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused ZeRO shard-step params/s + HBM GB/s (% of peak), 7.5B at N_d=64"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "zero_sharded_mixed_02_amd", "csrc", "zero_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_step_7p5B_nd64_traffic.json")
+
+DTYPE_NAME = {0: "fp32", 1: "fp16", 2: "bf16"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic_bytes_per_param(n_d: int, gdt_bytes: int = 2, pdt_bytes: int = 2) -> int:
+    """Bytes the fused step must move per shard element: n_d gradient reads,
+    fp32 master/m/v read and written, one 16-bit parameter written."""
+    return n_d * gdt_bytes + 3 * 4 * 2 + pdt_bytes
+
+
+def measured_traffic(launch_bytes: float):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source; None otherwise."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, n_sample: int):
+    """The oracle (single-threaded C) on a contiguous sample of the shard."""
+    import numpy as np
+    from oracle.runner import OracleRun
+    J = np.arange(n_sample, dtype=np.int64)
+    ref = OracleRun(cfg, sample=J)
+    t_check = cfg.steps
+    ref.fill_grads(t_check)
+    t0 = time.perf_counter()
+    ref.step(t_check)
+    dt = time.perf_counter() - t0
+    return {"value": n_sample / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n_sample} elements of the owner's shard, {cfg.n_d} "
+                      f"{DTYPE_NAME[cfg.gdt]} slices, one step (t={t_check}); {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--cpu-sample", type=int, default=1 << 22)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the step is one rank's share, and its "
+              "throughput at N GPUs is N times the one-GPU figure with no collective in the path; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from synth.workloads import CONFIGS, GpuRun
+    from __graft_entry__ import _ensure_built
+    _ensure_built()
+
+    cfg = CONFIGS[args.workload]
+    if cfg.stage == 3:
+        raise SystemExit("bench.py times the Stage-1/2 fused step; workload 5 is a parity case")
+    torch.cuda.init()
+    log(f"setting up {cfg.name}: psi={cfg.psi} n_d={cfg.n_d}")
+    run = GpuRun(cfg)
+    S = run.S
+    log(f"resident {run.bytes_resident() / 1e9:.1f} GB, shard {S}")
+    stream = torch.cuda.current_stream()
+
+    # Warm-up: fresh gradients for each of the first W steps.
+    t = 0
+    for _ in range(args.warmup):
+        t += 1
+        run.fill_grads(t)
+        run.step(t)
+    if args.warmup == 0:
+        run.fill_grads(1)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        t += 1
+        starts[i].record(stream)
+        run.step(t)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    total_ms = starts[0].elapsed_time(ends[-1])
+    ms_per_step = total_ms / args.steps
+    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    bpp = algorithmic_bytes_per_param(cfg.n_d)
+    launch_bytes = bpp * S
+    achieved = launch_bytes / avg_launch_s / 1e9
+    traffic = measured_traffic(launch_bytes)
+
+    out = {
+        "metric": METRIC,
+        "value": S / (ms_per_step / 1e3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "psi": cfg.psi, "n_d": cfg.n_d, "owner": cfg.owner,
+                   "shard_params": S, "grad_dtype": DTYPE_NAME[cfg.gdt],
+                   "param_dtype": DTYPE_NAME[cfg.pdt], "stage": cfg.stage},
+        "hbm_gbps": launch_bytes / (ms_per_step / 1e3) / 1e9,
+        "pct_of_hbm_peak": 100.0 * launch_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS,
+        "wall_s_timed": wall,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": launch_bytes,
+                     "avg_launch_ms": avg_launch_s * 1e3, "kernel": "step_vec_kernel (fused)"},
+    }
+    if args.no_cpu_baseline:
+        out["cpu_baseline"] = None
+    else:
+        del run
+        torch.cuda.empty_cache()
+        log("timing the CPU oracle on a sample ...")
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,36 @@
+"""ctypes wrapper of libsynth.so: GPU fills of the seeded synthetic inputs
+(definition in synth/__init__.py)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from . import _build, scale_for
+
+_lib = None
+
+
+def load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            raise ImportError(f"libsynth.so not built at {_build.LIB}")
+        L = ctypes.CDLL(_build.LIB)
+        L.synth_fill.restype = ctypes.c_int
+        L.synth_fill.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64,
+                                 ctypes.c_uint64, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                                 ctypes.c_void_p]
+        _lib = L
+    return _lib
+
+
+def fill(addr: int, dt: int, n: int, key: int, pos_base: int, sigma: float, stream: int,
+         mix: bool = False, sel_key: int = 0) -> None:
+    """Fill n elements at device address addr with the values at flat
+    positions pos_base .. pos_base + n - 1."""
+    if n <= 0:
+        return
+    err = load().synth_fill(ctypes.c_void_p(addr), dt, n, key, sel_key, 1 if mix else 0, pos_base,
+                            ctypes.c_float(float(scale_for(sigma))), ctypes.c_void_p(stream))
+    if err != 0:
+        raise RuntimeError(f"synth_fill failed with HIP error {err}")

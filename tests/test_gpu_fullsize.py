@@ -1,0 +1,92 @@
+"""Parity at the full workload sizes, in the launch configuration the
+benchmark times: the GPU runs the whole shard; the oracle computes a sample of
+its elements one by one (first and last 4096, every segment boundary, and
+random positions), which is exact because every operation of the step is
+elementwise in the shard index."""
+import numpy as np
+import pytest
+
+from synth.workloads import CONFIGS, GpuRun
+from tests.parity import assert_p16, assert_state
+
+pytestmark = [pytest.mark.gpu, pytest.mark.big]
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def sample_indices(S: int, seed: int, n_random: int = 65536) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    edges = [np.arange(min(4096, S)), np.arange(max(0, S - 4096), S)]
+    seg = 1 << 28
+    for b in range(seg, S, seg):            # pieces the host splits large shards into
+        edges.append(np.arange(b - 64, min(S, b + 64)))
+    edges.append(rng.integers(0, S, size=n_random))
+    return np.unique(np.concatenate(edges))
+
+
+def _free(run):
+    import torch
+    del run
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("num", [3, 4])
+def test_stage12_full_size(gpu, oracle_lib, num):
+    import torch
+    from oracle.runner import OracleRun
+    cfg = CONFIGS[num]
+    say(f"[full size] config {num} {cfg.name}: psi={cfg.psi} n_d={cfg.n_d} steps={cfg.steps}")
+    run = GpuRun(cfg)
+    say(f"  resident {run.bytes_resident() / 1e9:.1f} GB, S={run.S}")
+    J = sample_indices(run.S, seed=num)
+    ref = OracleRun(cfg, sample=J)
+    for t in range(1, cfg.steps + 1):
+        run.fill_grads(t)
+        ref.fill_grads(t)
+        run.step(t)
+        ref.step(t)
+        torch.cuda.synchronize()
+        say(f"  step {t} done")
+    got = run.fetch_at(J, ref.pos)
+    r = assert_state(got, ref.state(), cfg.pdt, cfg.name)
+    say(f"  sample of {J.size}: {r}")
+    _free(run)
+
+
+def test_stage3_full_size(gpu, oracle_lib):
+    import torch
+    import synth
+    from oracle.runner import OracleRun
+    cfg = CONFIGS[5]
+    say(f"[full size] config 5 {cfg.name}: {cfg.layers} layers of {cfg.psi} params, n_d={cfg.n_d}")
+    run = GpuRun(cfg)
+    say(f"  resident {run.bytes_resident() / 1e9:.1f} GB, S={run.S}")
+    J = sample_indices(run.S, seed=5)
+    ref = OracleRun(cfg, sample=J)
+    rng = np.random.default_rng(55)
+    flat_sample = np.unique(np.concatenate([np.arange(4096), np.arange(run.P - 4096, run.P),
+                                            rng.integers(0, run.P, 65536)]))
+    # Expected gathered values: the rank owning each position holds the 16-bit
+    # rounding of its master weight (how the resident shards were initialised).
+    pad = np.zeros(flat_sample.size, bool)
+    for bk in ref.plan.buckets:
+        pad |= (flat_sample >= bk.flat_off + bk.numel) & (flat_sample < bk.flat_off + bk.padded)
+    pos_t = torch.from_numpy(flat_sample).to(gpu)
+    for t in range(1, cfg.steps + 1):
+        for layer in range(cfg.layers):
+            run.fill_grads(t, layer)
+            ref.fill_grads(t, layer)
+            run.step(t, layer)
+            ref.step(t, layer)
+            torch.cuda.synchronize()
+            gathered = run.full[pos_t].cpu().numpy().view(np.uint16)
+            want = synth.to_dtype_bits(
+                synth.master_values(cfg.seed, flat_sample + layer * run.P, cfg.sigma_w, pad), cfg.pdt)
+            assert np.array_equal(gathered, want), ("gather", layer)
+            got = run.fetch_at(J, None, layer)
+            r = assert_state(got, ref.state(layer), cfg.pdt, f"layer {layer}")
+            say(f"  layer {layer}: gather ok, step {r['params']}")
+    _free(run)

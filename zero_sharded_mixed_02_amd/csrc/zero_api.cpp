@@ -1,0 +1,487 @@
+// zero_api.cpp -- host side of libzero.so: the plan, argument checks, launch
+// tables and the extern "C" entry points declared in include/zero.h.
+//
+// The plan follows the ZeRO pages' ownership convention (mind-map page,
+// "shrink the problem: four GPUs": rank i keeps the i-th contiguous block)
+// applied per bucket (concept page, design trade-off 1: collectives run over
+// buckets).  Nothing here allocates device memory; every kernel receives its
+// tables in its kernel arguments, split over several launches when a plan has
+// more pieces than one argument block holds.
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "zero.h"
+#include "zero_internal.h"
+
+#define ZERO_VERSION_NUMBER 100  // 0.1.0
+
+struct zero_plan_s {
+  int64_t psi = 0;
+  int32_t n_d = 1;
+  int64_t bucket_cap = 0;
+  int32_t align = 1;
+  int64_t psi_pad = 0;
+  int64_t shard_total = 0;
+  struct Bucket {
+    int64_t flat_off, numel, padded, shard_numel, shard_off;
+  };
+  std::vector<Bucket> buckets;
+  std::vector<int64_t> t_numel;
+  std::vector<int64_t> t_off;
+  std::vector<int32_t> t_bucket;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+zero_status fail(zero_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+zero_status ok() { return ZERO_OK; }
+
+int esize(int dt) { return dt == ZERO_F32 ? 4 : 2; }
+bool is16(int dt) { return dt == ZERO_F16 || dt == ZERO_BF16; }
+bool valid_dt(int dt) { return dt == ZERO_F32 || dt == ZERO_F16 || dt == ZERO_BF16; }
+
+struct Range {
+  uint64_t lo, hi;  // [lo, hi) bytes
+  const char* what;
+};
+
+Range range_of(const void* p, int64_t elems, int es, const char* what) {
+  const uint64_t lo = (uint64_t)(uintptr_t)p;
+  return Range{lo, lo + (uint64_t)elems * (uint64_t)es, what};
+}
+
+bool overlap(const Range& a, const Range& b) {
+  if (a.hi == a.lo || b.hi == b.lo) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, int bytes) { return ((uintptr_t)p % (uintptr_t)bytes) == 0; }
+
+zero_status hip_fail(int err) {
+  return fail(ZERO_EHIP, "HIP launch failed: %s (%d)", zk::hip_error_string(err), err);
+}
+
+// The nine fp32 constants of step t, rounded once from fp64.
+void adam_consts(const zero_adam_hyper& h, int64_t t, float c[9]) {
+  c[0] = (float)h.beta1;
+  c[1] = (float)(1.0 - h.beta1);
+  c[2] = (float)h.beta2;
+  c[3] = (float)(1.0 - h.beta2);
+  c[4] = (float)(1.0 - std::pow(h.beta1, (double)t));
+  c[5] = (float)(1.0 - std::pow(h.beta2, (double)t));
+  c[6] = (float)h.lr;
+  c[7] = (float)h.eps;
+  c[8] = (float)h.grad_scale;
+}
+
+// One piece of the owner's shard, before it is packed into a launch.
+struct Piece {
+  int64_t shard_off, full_off, dst_off, len;
+};
+
+std::vector<Piece> owner_pieces(const zero_plan_s& p, int32_t rank, bool dst_full) {
+  std::vector<Piece> out;
+  for (const auto& b : p.buckets) {
+    const int64_t own = b.flat_off + (int64_t)rank * b.shard_numel;
+    for (int64_t k = 0; k < b.shard_numel; k += zk::kSegMaxElems) {
+      const int64_t len = std::min<int64_t>(zk::kSegMaxElems, b.shard_numel - k);
+      out.push_back(Piece{b.shard_off + k, own + k, (dst_full ? own : b.shard_off) + k, len});
+    }
+  }
+  return out;
+}
+
+bool pieces_vectorisable(const std::vector<Piece>& ps) {
+  for (const auto& q : ps)
+    if ((q.shard_off | q.full_off | q.dst_off | q.len) & 7) return false;
+  return true;
+}
+
+int ndc_for(int n) { return (n == 4 || n == 8 || n == 16 || n == 64) ? n : 0; }
+
+// Launch the step kernel over all pieces, in chunks of kMaxSeg.
+zero_status run_step(zk::StepArgs& a, const std::vector<Piece>& ps, int mode, int gdt, int pdt,
+                     bool vec, void* stream) {
+  const int per_block = zk::kThreads * (vec ? zk::kStepVec : 1);
+  size_t i = 0;
+  while (i < ps.size()) {
+    int nseg = 0;
+    int64_t blocks = 0;
+    for (; i < ps.size() && nseg < zk::kMaxSeg; ++i) {
+      const Piece& q = ps[i];
+      const int64_t nb = (q.len + per_block - 1) / per_block;
+      if (blocks + nb > INT32_MAX) break;
+      zk::StepSeg& s = a.seg[nseg++];
+      s.shard_off = q.shard_off;
+      s.full_off = q.full_off;
+      s.dst_off = q.dst_off;
+      s.len = (int32_t)q.len;
+      s.block_start = (int32_t)blocks;
+      blocks += nb;
+    }
+    a.n_seg = nseg;
+    if (blocks == 0) continue;
+    const int err = zk::launch_step(a, mode, gdt, pdt, ndc_for(a.n_ranks), vec, (int)blocks, stream);
+    if (err != 0) return hip_fail(err);
+  }
+  return ok();
+}
+
+// Fill the rank table of a step launch with ranks [q0, q0 + n).
+void set_ranks(zk::StepArgs& a, const zero_plan_s& p, const zero_grad_src& src, int q0, int n) {
+  memset(a.grad, 0, sizeof a.grad);
+  memset(a.full_mask, 0, sizeof a.full_mask);
+  for (int i = 0; i < n; ++i) {
+    a.grad[i] = src.ptrs[q0 + i];
+    if (src.is_full && src.is_full[q0 + i]) a.full_mask[i >> 5] |= 1u << (i & 31);
+  }
+  a.n_ranks = n;
+  (void)p;
+}
+
+// Common checks of a gradient source; collects the read ranges.
+zero_status check_src(const zero_plan_s& p, const zero_grad_src* src, std::vector<Range>& reads,
+                      bool& all16aligned) {
+  if (!src) return fail(ZERO_EINVAL, "gradient source is NULL");
+  if (src->n != p.n_d) return fail(ZERO_EINVAL, "gradient source has %d ranks, plan has n_d=%d", src->n, p.n_d);
+  if (!src->ptrs) return fail(ZERO_EINVAL, "gradient pointer array is NULL");
+  if (!is16(src->dtype)) return fail(ZERO_EUNSUPPORTED, "gradient dtype %d is not 16-bit", src->dtype);
+  for (int q = 0; q < src->n; ++q) {
+    const void* g = src->ptrs[q];
+    const bool full = src->is_full && src->is_full[q];
+    const int64_t n = full ? p.psi_pad : p.shard_total;
+    if (!g && n > 0) return fail(ZERO_EINVAL, "gradient pointer of rank %d is NULL", q);
+    if (!aligned(g, 2)) return fail(ZERO_EINVAL, "gradient of rank %d is not 2-byte aligned", q);
+    if (!aligned(g, 16)) all16aligned = false;
+    reads.push_back(range_of(g, n, 2, "gradient"));
+  }
+  return ok();
+}
+
+zero_status check_plan(zero_plan_t p) {
+  if (!p) return fail(ZERO_EINVAL, "plan is NULL");
+  return ok();
+}
+
+// Copy entries -> launches of kMaxCopy entries.
+zero_status run_copies(std::vector<zk::CopyEnt>& ents, void* dst, int es, void* stream) {
+  zk::CopyArgs a;
+  memset(&a, 0, sizeof a);
+  a.dst = dst;
+  const int64_t units_per_block = (int64_t)zk::kThreads * zk::kCopyUnits;
+  size_t i = 0;
+  while (i < ents.size()) {
+    int n = 0;
+    int64_t blocks = 0;
+    for (; i < ents.size() && n < zk::kMaxCopy; ++i) {
+      const zk::CopyEnt& e = ents[i];
+      if (e.n == 0) continue;
+      const uint64_t d0 = (uint64_t)(uintptr_t)dst + (uint64_t)e.dst_off * es;
+      const uint64_t d1 = d0 + (uint64_t)e.n * es;
+      const int64_t units = (int64_t)(((d1 + 15) >> 4) - (d0 >> 4));
+      const int64_t nb = (units + units_per_block - 1) / units_per_block;
+      if (blocks + nb > INT32_MAX) break;
+      a.ent[n] = e;
+      a.ent[n].block_start = (int32_t)blocks;
+      ++n;
+      blocks += nb;
+    }
+    a.n_ent = n;
+    if (n == 0) continue;
+    const int err = zk::launch_copy(a, es, (int)blocks, stream);
+    if (err != 0) return hip_fail(err);
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t zero_version(void) { return ZERO_VERSION_NUMBER; }
+
+const char* zero_last_error(void) { return g_err.c_str(); }
+
+zero_status zero_plan(int64_t psi, int32_t n_d, const int64_t* tensor_numel, int32_t n_tensors,
+                      int64_t bucket_cap, int32_t shard_align, zero_plan_t* out) {
+  try {
+    if (!out) return fail(ZERO_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (n_d < 1) return fail(ZERO_EINVAL, "n_d must be >= 1 (got %d)", n_d);
+    if (shard_align < 1) return fail(ZERO_EINVAL, "shard_align must be >= 1 (got %d)", shard_align);
+    if (bucket_cap < 0) return fail(ZERO_EINVAL, "bucket_cap must be >= 0");
+    if (n_tensors < 0) return fail(ZERO_EINVAL, "n_tensors must be >= 0");
+    if (n_tensors > 0 && !tensor_numel) return fail(ZERO_EINVAL, "tensor_numel is NULL");
+    if (psi < 0) return fail(ZERO_EINVAL, "psi must be >= 0");
+    int64_t sum = 0;
+    for (int32_t t = 0; t < n_tensors; ++t) {
+      if (tensor_numel[t] < 0) return fail(ZERO_EINVAL, "tensor %d has negative size", t);
+      if (tensor_numel[t] > INT64_MAX / 4 - sum) return fail(ZERO_EINVAL, "tensor sizes overflow");
+      sum += tensor_numel[t];
+    }
+    if (sum != psi)
+      return fail(ZERO_EINVAL, "tensor sizes sum to %lld, psi is %lld", (long long)sum, (long long)psi);
+    const int64_t unit = (int64_t)n_d * shard_align;
+
+    zero_plan_s* p = new zero_plan_s();
+    p->psi = psi;
+    p->n_d = n_d;
+    p->bucket_cap = bucket_cap;
+    p->align = shard_align;
+    p->t_numel.assign(tensor_numel, tensor_numel + n_tensors);
+    p->t_off.resize(n_tensors);
+    p->t_bucket.resize(n_tensors);
+
+    // Greedy list-order bucketing: close the open bucket when the next tensor
+    // would take it past the cap.
+    int64_t flat = 0, shard = 0, open_numel = 0;
+    bool open = false;
+    auto close_bucket = [&]() {
+      const int64_t padded = (open_numel + unit - 1) / unit * unit;
+      const int64_t sn = padded / n_d;
+      p->buckets.push_back({flat, open_numel, padded, sn, shard});
+      flat += padded;
+      shard += sn;
+      open = false;
+      open_numel = 0;
+    };
+    for (int32_t t = 0; t < n_tensors; ++t) {
+      const int64_t n = tensor_numel[t];
+      if (open && bucket_cap > 0 && open_numel + n > bucket_cap) close_bucket();
+      p->t_bucket[t] = (int32_t)p->buckets.size();
+      p->t_off[t] = flat + open_numel;
+      open_numel += n;
+      open = true;
+    }
+    if (open) close_bucket();
+    p->psi_pad = flat;
+    p->shard_total = shard;
+    *out = p;
+    return ok();
+  } catch (const std::bad_alloc&) {
+    return fail(ZERO_ENOMEM, "host allocation failed");
+  } catch (...) {
+    return fail(ZERO_EINVAL, "unexpected failure in zero_plan");
+  }
+}
+
+void zero_plan_destroy(zero_plan_t plan) { delete plan; }
+
+zero_status zero_plan_info(zero_plan_t p, int64_t* psi_pad, int64_t* shard_total, int32_t* n_buckets,
+                           int32_t* n_d) {
+  if (check_plan(p)) return ZERO_EINVAL;
+  if (psi_pad) *psi_pad = p->psi_pad;
+  if (shard_total) *shard_total = p->shard_total;
+  if (n_buckets) *n_buckets = (int32_t)p->buckets.size();
+  if (n_d) *n_d = p->n_d;
+  return ok();
+}
+
+zero_status zero_plan_bucket(zero_plan_t p, int32_t b, int64_t* flat_off, int64_t* numel,
+                             int64_t* padded, int64_t* shard_numel, int64_t* shard_off) {
+  if (check_plan(p)) return ZERO_EINVAL;
+  if (b < 0 || b >= (int32_t)p->buckets.size()) return fail(ZERO_EINVAL, "bucket %d out of range", b);
+  const auto& k = p->buckets[b];
+  if (flat_off) *flat_off = k.flat_off;
+  if (numel) *numel = k.numel;
+  if (padded) *padded = k.padded;
+  if (shard_numel) *shard_numel = k.shard_numel;
+  if (shard_off) *shard_off = k.shard_off;
+  return ok();
+}
+
+zero_status zero_plan_tensor(zero_plan_t p, int32_t t, int32_t* bucket, int64_t* flat_off) {
+  if (check_plan(p)) return ZERO_EINVAL;
+  if (t < 0 || t >= (int32_t)p->t_numel.size()) return fail(ZERO_EINVAL, "tensor %d out of range", t);
+  if (bucket) *bucket = p->t_bucket[t];
+  if (flat_off) *flat_off = p->t_off[t];
+  return ok();
+}
+
+zero_status zero_flatten(zero_plan_t p, const void* const* tensors, zero_dtype dt, void* flat,
+                         void* stream) {
+  try {
+    if (check_plan(p)) return ZERO_EINVAL;
+    if (!valid_dt(dt)) return fail(ZERO_EINVAL, "unknown dtype %d", (int)dt);
+    const int es = esize(dt);
+    const int32_t nt = (int32_t)p->t_numel.size();
+    if (nt > 0 && !tensors) return fail(ZERO_EINVAL, "tensor pointer array is NULL");
+    if (!flat && p->psi_pad > 0) return fail(ZERO_EINVAL, "flat is NULL");
+    if (!aligned(flat, es)) return fail(ZERO_EINVAL, "flat is not element aligned");
+    const Range out = range_of(flat, p->psi_pad, es, "flat");
+    std::vector<zk::CopyEnt> ents;
+    ents.reserve(nt + p->buckets.size());
+    for (int32_t t = 0; t < nt; ++t) {
+      const int64_t n = p->t_numel[t];
+      if (n == 0) continue;
+      if (!tensors[t]) return fail(ZERO_EINVAL, "tensor %d is NULL", t);
+      if (!aligned(tensors[t], es)) return fail(ZERO_EINVAL, "tensor %d is not element aligned", t);
+      if (overlap(out, range_of(tensors[t], n, es, "tensor")))
+        return fail(ZERO_EINVAL, "flat overlaps tensor %d", t);
+      ents.push_back(zk::CopyEnt{tensors[t], p->t_off[t], n, 0, 0});
+    }
+    for (const auto& b : p->buckets)   // zero padding at each bucket's end
+      if (b.padded > b.numel) ents.push_back(zk::CopyEnt{nullptr, b.flat_off + b.numel, b.padded - b.numel, 0, 0});
+    return run_copies(ents, flat, es, stream);
+  } catch (const std::bad_alloc&) {
+    return fail(ZERO_ENOMEM, "host allocation failed");
+  } catch (...) {
+    return fail(ZERO_EINVAL, "unexpected failure in zero_flatten");
+  }
+}
+
+zero_status zero_gather_pack(zero_plan_t p, const void* const* shards, zero_dtype dt, void* full,
+                             void* stream) {
+  try {
+    if (check_plan(p)) return ZERO_EINVAL;
+    if (!valid_dt(dt)) return fail(ZERO_EINVAL, "unknown dtype %d", (int)dt);
+    const int es = esize(dt);
+    if (!shards) return fail(ZERO_EINVAL, "shard pointer array is NULL");
+    if (!full && p->psi_pad > 0) return fail(ZERO_EINVAL, "full is NULL");
+    if (!aligned(full, es)) return fail(ZERO_EINVAL, "full is not element aligned");
+    const Range out = range_of(full, p->psi_pad, es, "full");
+    for (int32_t q = 0; q < p->n_d; ++q) {
+      if (!shards[q] && p->shard_total > 0) return fail(ZERO_EINVAL, "shard %d is NULL", q);
+      if (!aligned(shards[q], es)) return fail(ZERO_EINVAL, "shard %d is not element aligned", q);
+      if (overlap(out, range_of(shards[q], p->shard_total, es, "shard")))
+        return fail(ZERO_EINVAL, "full overlaps shard %d", q);
+    }
+    std::vector<zk::CopyEnt> ents;
+    ents.reserve((size_t)p->n_d * p->buckets.size());
+    for (const auto& b : p->buckets)
+      for (int32_t q = 0; q < p->n_d; ++q)
+        ents.push_back(zk::CopyEnt{(const char*)shards[q] + b.shard_off * es,
+                                   b.flat_off + (int64_t)q * b.shard_numel, b.shard_numel, 0, 0});
+    return run_copies(ents, full, es, stream);
+  } catch (const std::bad_alloc&) {
+    return fail(ZERO_ENOMEM, "host allocation failed");
+  } catch (...) {
+    return fail(ZERO_EINVAL, "unexpected failure in zero_gather_pack");
+  }
+}
+
+zero_status zero_shard_reduce(zero_plan_t p, int32_t rank, const zero_grad_src* src,
+                              double grad_scale, float* out, void* stream) {
+  try {
+    if (check_plan(p)) return ZERO_EINVAL;
+    if (rank < 0 || rank >= p->n_d) return fail(ZERO_EINVAL, "rank %d outside [0, %d)", rank, p->n_d);
+    std::vector<Range> reads;
+    bool al16 = true;
+    if (zero_status st = check_src(*p, src, reads, al16)) return st;
+    if (!out && p->shard_total > 0) return fail(ZERO_EINVAL, "out is NULL");
+    if (!aligned(out, 4)) return fail(ZERO_EINVAL, "out is not 4-byte aligned");
+    if (!aligned(out, 16)) al16 = false;
+    const Range w = range_of(out, p->shard_total, 4, "out");
+    for (const auto& r : reads)
+      if (overlap(w, r)) return fail(ZERO_EINVAL, "out overlaps a gradient buffer");
+
+    const std::vector<Piece> ps = owner_pieces(*p, rank, false);
+    const bool vec = al16 && pieces_vectorisable(ps);
+    zk::StepArgs a;
+    memset(&a, 0, sizeof a);
+    a.out = out;
+    a.c[8] = (float)grad_scale;
+    // Ranks beyond one launch's table: later launches continue from out.
+    for (int q0 = 0; q0 < p->n_d; q0 += zk::kMaxRanks) {
+      const int n = std::min(zk::kMaxRanks, p->n_d - q0);
+      set_ranks(a, *p, *src, q0, n);
+      a.flags = (q0 > 0 ? zk::kFlagInitFromOut : 0) | (q0 + n == p->n_d ? zk::kFlagApplyScale : 0);
+      if (zero_status st = run_step(a, ps, zk::kReduceOnly, src->dtype, ZERO_F16, vec, stream)) return st;
+    }
+    return ok();
+  } catch (const std::bad_alloc&) {
+    return fail(ZERO_ENOMEM, "host allocation failed");
+  } catch (...) {
+    return fail(ZERO_EINVAL, "unexpected failure in zero_shard_reduce");
+  }
+}
+
+zero_status zero_adam_step(zero_plan_t p, int32_t rank, const zero_adam_hyper* hp, int64_t t,
+                           const zero_grad_src* slices, const float* reduced, float* master,
+                           float* m, float* v, void* param_dst, zero_dtype param_dt,
+                           int32_t dst_is_full, void* stream) {
+  try {
+    if (check_plan(p)) return ZERO_EINVAL;
+    if (rank < 0 || rank >= p->n_d) return fail(ZERO_EINVAL, "rank %d outside [0, %d)", rank, p->n_d);
+    if (!hp) return fail(ZERO_EINVAL, "hyper-parameters are NULL");
+    if (t < 1) return fail(ZERO_EINVAL, "step t must be >= 1 (got %lld)", (long long)t);
+    if (!is16(param_dt)) return fail(ZERO_EUNSUPPORTED, "parameter dtype %d is not 16-bit", (int)param_dt);
+    const int64_t S = p->shard_total;
+    const int64_t dst_elems = dst_is_full ? p->psi_pad : S;
+    std::vector<Range> reads;
+    bool al16 = true;
+    if (slices) {
+      if (p->n_d > zk::kMaxRanks)
+        return fail(ZERO_EUNSUPPORTED, "fused step reads at most %d ranks; use zero_shard_reduce and pass reduced",
+                    zk::kMaxRanks);
+      if (zero_status st = check_src(*p, slices, reads, al16)) return st;
+    } else {
+      if (!reduced && S > 0) return fail(ZERO_EINVAL, "both slices and reduced are NULL");
+      if (!aligned(reduced, 4)) return fail(ZERO_EINVAL, "reduced is not 4-byte aligned");
+      if (!aligned(reduced, 16)) al16 = false;
+      reads.push_back(range_of(reduced, S, 4, "reduced"));
+    }
+    float* const st_ptr[3] = {master, m, v};
+    const char* st_name[3] = {"master", "m", "v"};
+    std::vector<Range> writes;
+    for (int i = 0; i < 3; ++i) {
+      if (!st_ptr[i] && S > 0) return fail(ZERO_EINVAL, "%s is NULL", st_name[i]);
+      if (!aligned(st_ptr[i], 4)) return fail(ZERO_EINVAL, "%s is not 4-byte aligned", st_name[i]);
+      if (!aligned(st_ptr[i], 16)) al16 = false;
+      writes.push_back(range_of(st_ptr[i], S, 4, st_name[i]));
+    }
+    if (!param_dst && dst_elems > 0) return fail(ZERO_EINVAL, "param_dst is NULL");
+    if (!aligned(param_dst, 2)) return fail(ZERO_EINVAL, "param_dst is not 2-byte aligned");
+    if (!aligned(param_dst, 16)) al16 = false;
+    writes.push_back(range_of(param_dst, dst_elems, 2, "param_dst"));
+    for (size_t i = 0; i < writes.size(); ++i) {
+      for (size_t j = i + 1; j < writes.size(); ++j)
+        if (overlap(writes[i], writes[j]))
+          return fail(ZERO_EINVAL, "%s overlaps %s", writes[i].what, writes[j].what);
+      for (const auto& r : reads)
+        if (overlap(writes[i], r)) return fail(ZERO_EINVAL, "%s overlaps %s", writes[i].what, r.what);
+    }
+
+    const std::vector<Piece> ps = owner_pieces(*p, rank, dst_is_full != 0);
+    const bool vec = al16 && pieces_vectorisable(ps);
+    zk::StepArgs a;
+    memset(&a, 0, sizeof a);
+    adam_consts(*hp, t, a.c);
+    a.master = master;
+    a.m = m;
+    a.v = v;
+    a.dst = param_dst;
+    if (slices) {
+      set_ranks(a, *p, *slices, 0, p->n_d);
+      return run_step(a, ps, zk::kFused, slices->dtype, param_dt, vec, stream);
+    }
+    a.reduced = reduced;
+    a.n_ranks = 0;
+    return run_step(a, ps, zk::kFromReduced, ZERO_BF16, param_dt, vec, stream);
+  } catch (const std::bad_alloc&) {
+    return fail(ZERO_ENOMEM, "host allocation failed");
+  } catch (...) {
+    return fail(ZERO_EINVAL, "unexpected failure in zero_adam_step");
+  }
+}
+
+}  // extern "C"

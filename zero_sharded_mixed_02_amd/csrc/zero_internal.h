@@ -1,0 +1,85 @@
+// zero_internal.h -- structures shared by the host launcher and the gfx950
+// kernels of libzero.so.  Everything a kernel needs travels in its kernel
+// arguments (no device-side tables, no allocation): per-launch tables are
+// capped so the argument block stays under 4 KiB, and larger plans are
+// covered by several launches.
+#pragma once
+
+#include <stdint.h>
+
+#include "zero.h"
+
+namespace zk {
+
+constexpr int kMaxRanks = ZERO_MAX_RANKS;   // gradient pointers per launch
+constexpr int kMaxSeg = 64;                  // shard segments per step launch
+constexpr int kMaxCopy = 112;                // copy entries per copy launch
+constexpr int64_t kSegMaxElems = int64_t(1) << 28;  // keeps per-lane byte offsets in 32 bits
+
+constexpr int kThreads = 256;               // 4 wave64s per workgroup
+constexpr int kStepVec = 8;                 // elements per lane in the vector step kernel
+constexpr int kCopyUnits = 4;               // 16-byte units per lane in the copy kernel
+
+// One contiguous piece of the owner's shard (a bucket's slice, or part of it).
+struct StepSeg {
+  int64_t shard_off;    // element offset in the shard-local arrays (state, compact grads)
+  int64_t full_off;     // element offset in a full gradient buffer (Stage 1)
+  int64_t dst_off;      // element offset in the parameter destination
+  int32_t len;          // elements, <= kSegMaxElems
+  int32_t block_start;  // first workgroup of this piece in the launch
+};
+
+enum StepMode : int {
+  kFused = 0,        // reduce ranks in registers, then Adam, cast, store
+  kFromReduced = 1,  // Adam reading an fp32 reduced gradient
+  kReduceOnly = 2    // fold ranks, write fp32
+};
+
+enum StepFlags : int {
+  kFlagInitFromOut = 1,   // reduce: continue the fold from the fp32 output
+  kFlagApplyScale = 2     // reduce: multiply by grad_scale at the end
+};
+
+struct StepArgs {
+  const void* grad[kMaxRanks];
+  uint32_t full_mask[kMaxRanks / 32];
+  const float* reduced;   // kFromReduced input
+  float* out;             // kReduceOnly output
+  float* master;
+  float* m;
+  float* v;
+  void* dst;
+  float c[9];             // b1, 1-b1, b2, 1-b2, 1-b1^t, 1-b2^t, lr, eps, grad_scale
+  int32_t n_ranks;
+  int32_t n_seg;
+  int32_t flags;
+  int32_t pad_;
+  StepSeg seg[kMaxSeg];
+};
+
+// One copy: n elements from src (nullptr = zeros) to dst + dst_off.
+struct CopyEnt {
+  const void* src;
+  int64_t dst_off;
+  int64_t n;
+  int32_t block_start;
+  int32_t pad_;
+};
+
+struct CopyArgs {
+  void* dst;
+  int32_t n_ent;
+  int32_t pad_;
+  CopyEnt ent[kMaxCopy];
+};
+
+static_assert(sizeof(StepArgs) <= 4096, "step kernel arguments must fit 4 KiB");
+static_assert(sizeof(CopyArgs) <= 4096, "copy kernel arguments must fit 4 KiB");
+
+// Kernel launchers (zero_kernels.hip).  Return a hipError_t as int.
+int launch_step(const StepArgs& a, int mode, int gdt, int pdt, int ndc, bool vec, int n_blocks,
+                void* stream);
+int launch_copy(const CopyArgs& a, int esz, int n_blocks, void* stream);
+const char* hip_error_string(int err);
+
+}  // namespace zk

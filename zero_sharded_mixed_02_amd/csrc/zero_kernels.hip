@@ -1,0 +1,485 @@
+// zero_kernels.hip -- gfx950 kernels of the ZeRO shard step.
+//
+// Two kernel families, both bound by HBM bandwidth and written for CDNA4's
+// 64-lane wavefronts (no MFMA: nothing here is a contraction):
+//
+//  * step kernels: for each element of the owner's shard, fold the N_d ranks'
+//    16-bit gradient contributions in fixed rank order in fp32 (the
+//    arithmetic of reduce-scatter), then run the mixed-precision Adam update on
+//    the fp32 master weight and moments and store the rounded 16-bit parameter
+//    into the all-gather buffer -- all in registers, one HBM pass.  In the
+//    vector kernel each lane owns 8 consecutive elements: one 16-byte load per
+//    rank, two per fp32 state array, one 16-byte parameter store.  Every rank
+//    pointer and segment offset is wave-uniform, so address arithmetic stays on
+//    the scalar unit and vector accesses are an SGPR base plus a 32-bit lane
+//    offset.
+//
+//  * copy kernel: destination-aligned 16-byte copies used by flatten (ragged
+//    tensors into padded buckets, at any element offset) and gather_pack
+//    (shards into the full buffer).  A misaligned source is realigned in
+//    registers with byte funnel shifts; partial units at the ends of an entry
+//    are copied element by element, so no byte outside an entry is touched.
+//
+// Floating point: compiled with -ffp-contract=off; fp32 division and square
+// root are HIP's correctly rounded defaults; denormals are preserved.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zero_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace zk {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+// Global-address-space views, so that accesses are global_* (not flat_*).
+typedef __attribute__((address_space(1))) u32x4 gu32x4;
+typedef __attribute__((address_space(1))) f32x4 gf32x4;
+typedef __attribute__((address_space(1))) uint16_t gu16;
+typedef __attribute__((address_space(1))) uint32_t gu32;
+typedef __attribute__((address_space(1))) float gf32;
+
+template <typename T>
+__device__ __forceinline__ T gaddr(const void* p) {
+  return (T)p;
+}
+template <typename T>
+__device__ __forceinline__ T gaddr(uint64_t p) {
+  return (T)(uintptr_t)p;
+}
+
+// Streaming (non-temporal) accesses: every byte of the step is touched once.
+__device__ __forceinline__ u32x4 ld_nt(const gu32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ f32x4 ld_nt(const gf32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void st_nt(gu32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void st_nt(gf32x4* p, f32x4 v) { __builtin_nontemporal_store(v, p); }
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// 8 packed 16-bit values -> 8 fp32 values (exact widening).
+template <int GDT>
+__device__ __forceinline__ void widen8(const u32x4 r, float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (GDT == ZERO_BF16) {
+      x[2 * i] = __uint_as_float(r[i] << 16);
+      x[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+    } else {
+      x[2 * i] = f16_bits_to_f32(r[i] & 0xffffu);
+      x[2 * i + 1] = f16_bits_to_f32(r[i] >> 16);
+    }
+  }
+}
+
+template <int GDT>
+__device__ __forceinline__ float widen1(uint32_t h) {
+  if constexpr (GDT == ZERO_BF16) return __uint_as_float(h << 16);
+  else return f16_bits_to_f32(h);
+}
+
+// fp32 -> 16-bit, round to nearest even (gfx950 conversion instructions).
+template <int PDT>
+__device__ __forceinline__ uint32_t narrow1(float x) {
+  if constexpr (PDT == ZERO_BF16) return __builtin_bit_cast(uint16_t, (__bf16)x);
+  else return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+struct AdamC {
+  float b1, c1, b2, c2, bc1, bc2, lr, eps, gs;
+};
+
+__device__ __forceinline__ AdamC load_consts(const StepArgs& a) {
+  return AdamC{a.c[0], a.c[1], a.c[2], a.c[3], a.c[4], a.c[5], a.c[6], a.c[7], a.c[8]};
+}
+
+// Textbook Adam on one element (bias-corrected moments, eps outside the
+// square root, no weight decay).  One fp32 operation per statement.
+__device__ __forceinline__ void adam1(const AdamC& k, float g, float& w, float& m, float& v) {
+  const float m_old = k.b1 * m;
+  const float m_in = k.c1 * g;
+  m = m_old + m_in;
+  const float g2 = g * g;
+  const float v_old = k.b2 * v;
+  const float v_in = k.c2 * g2;
+  v = v_old + v_in;
+  const float mh = m / k.bc1;
+  const float vh = v / k.bc2;
+  const float root = __builtin_sqrtf(vh);
+  const float den = root + k.eps;
+  const float upd = mh / den;
+  const float delta = k.lr * upd;
+  w = w - delta;
+}
+
+// Segment handled by this workgroup (wave-uniform linear scan, <= 64 entries).
+__device__ __forceinline__ int find_seg(const StepArgs& a, int blk) {
+  int s = 0;
+  for (int i = 1; i < a.n_seg; ++i)
+    if (a.seg[i].block_start <= blk) s = i;
+  return s;
+}
+
+// Byte address of rank q's contribution at the segment's first element.
+__device__ __forceinline__ uint64_t rank_base(const StepArgs& a, int q, int64_t shard_off,
+                                              int64_t full_off) {
+  const bool full = (a.full_mask[q >> 5] >> (q & 31)) & 1u;
+  return (uint64_t)(uintptr_t)a.grad[q] + (uint64_t)((full ? full_off : shard_off) * 2);
+}
+
+__device__ __forceinline__ const gu32x4* grad_vec(const StepArgs& a, int q, int64_t shard_off,
+                                                  int64_t full_off, uint32_t boff) {
+  return gaddr<const gu32x4*>(rank_base(a, q, shard_off, full_off)) + (boff >> 4);
+}
+
+// Fold the launch's ranks for 8 consecutive elements at byte offset boff of
+// each rank's segment base.  CONT = false: the fold starts from rank 0's value;
+// CONT = true: every rank is added to the incoming acc (continuing a fold
+// begun by an earlier launch).  Loads are issued in batches of B ranks ahead
+// of their adds so that B KiB per wave are in flight; adds keep rank order.
+template <int GDT, int NDC, bool CONT>
+__device__ __forceinline__ void fold8(const StepArgs& a, int64_t shard_off, int64_t full_off,
+                                      uint32_t boff, float (&acc)[8]) {
+  if constexpr (NDC > 0) {
+    constexpr int B = NDC < 16 ? NDC : 16;
+#pragma unroll
+    for (int q0 = 0; q0 < NDC; q0 += B) {
+      u32x4 raw[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) raw[i] = ld_nt(grad_vec(a, q0 + i, shard_off, full_off, boff));
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        float x[8];
+        widen8<GDT>(raw[i], x);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] = (!CONT && q0 + i == 0) ? x[k] : acc[k] + x[k];
+      }
+    }
+  } else {
+    const int n = a.n_ranks;
+    int q = 0;
+    if (!CONT) {
+      float x[8];
+      widen8<GDT>(ld_nt(grad_vec(a, 0, shard_off, full_off, boff)), x);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = x[k];
+      q = 1;
+    }
+    constexpr int B = 8;
+    for (; q + B <= n; q += B) {
+      u32x4 raw[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) raw[i] = ld_nt(grad_vec(a, q + i, shard_off, full_off, boff));
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        float x[8];
+        widen8<GDT>(raw[i], x);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] = acc[k] + x[k];
+      }
+    }
+    for (; q < n; ++q) {
+      float x[8];
+      widen8<GDT>(ld_nt(grad_vec(a, q, shard_off, full_off, boff)), x);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = acc[k] + x[k];
+    }
+  }
+}
+
+__device__ __forceinline__ void load8(const gf32x4* p, float (&x)[8]) {
+  const f32x4 a = ld_nt(p), b = ld_nt(p + 1);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[k] = a[k];
+    x[4 + k] = b[k];
+  }
+}
+
+__device__ __forceinline__ void store8(gf32x4* p, const float (&x)[8]) {
+  f32x4 a, b;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    a[k] = x[k];
+    b[k] = x[4 + k];
+  }
+  st_nt(p, a);
+  st_nt(p + 1, b);
+}
+
+// Vector kernel: 8 elements per lane.  The host takes this kernel only when
+// every segment offset and length is a multiple of 8 elements and every base
+// address is 16-byte aligned.
+template <int MODE, int GDT, int PDT, int NDC>
+__global__ void __launch_bounds__(kThreads) step_vec_kernel(const StepArgs a) {
+  const int blk = blockIdx.x;
+  const int s = find_seg(a, blk);
+  const int64_t shard_off = a.seg[s].shard_off;
+  const int64_t full_off = a.seg[s].full_off;
+  const int64_t dst_off = a.seg[s].dst_off;
+  const uint32_t len = (uint32_t)a.seg[s].len;
+  const uint32_t e = (uint32_t)(blk - a.seg[s].block_start) * (kThreads * kStepVec) +
+                     threadIdx.x * kStepVec;
+  if (e >= len) return;
+
+  float g[8];
+  if constexpr (MODE == kFromReduced) {
+    load8(gaddr<const gf32x4*>(a.reduced + shard_off) + (e >> 2), g);
+  } else if constexpr (MODE == kFused) {
+    float acc[8];
+    fold8<GDT, NDC, false>(a, shard_off, full_off, e * 2u, acc);
+    const float gs = a.c[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) g[k] = acc[k] * gs;
+  } else {  // kReduceOnly
+    gf32x4* op = gaddr<gf32x4*>(a.out + shard_off) + (e >> 2);
+    float acc[8];
+    if (a.flags & kFlagInitFromOut) {
+      // The fp32 prefix of the fold was stored exactly by the previous launch.
+      load8(op, acc);
+      fold8<GDT, NDC, true>(a, shard_off, full_off, e * 2u, acc);
+    } else {
+      fold8<GDT, NDC, false>(a, shard_off, full_off, e * 2u, acc);
+    }
+    if (a.flags & kFlagApplyScale) {
+      const float gs = a.c[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = acc[k] * gs;
+    }
+    store8(op, acc);
+  }
+
+  if constexpr (MODE != kReduceOnly) {
+    const AdamC k = load_consts(a);
+    gf32x4* wp = gaddr<gf32x4*>(a.master + shard_off) + (e >> 2);
+    gf32x4* mp = gaddr<gf32x4*>(a.m + shard_off) + (e >> 2);
+    gf32x4* vp = gaddr<gf32x4*>(a.v + shard_off) + (e >> 2);
+    float w[8], m[8], v[8];
+    load8(wp, w);
+    load8(mp, m);
+    load8(vp, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) adam1(k, g[i], w[i], m[i], v[i]);
+    u32x4 p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = narrow1<PDT>(w[2 * i]) | (narrow1<PDT>(w[2 * i + 1]) << 16);
+    store8(wp, w);
+    store8(mp, m);
+    store8(vp, v);
+    st_nt(gaddr<gu32x4*>((uint16_t*)a.dst + dst_off) + (e >> 3), p);
+  }
+}
+
+// Element kernel: one element per lane, any element alignment (taken when a
+// plan's offsets are not multiples of 8 elements or a base is not 16-byte
+// aligned).
+template <int MODE, int GDT, int PDT>
+__global__ void __launch_bounds__(kThreads) step_elem_kernel(const StepArgs a) {
+  const int blk = blockIdx.x;
+  const int s = find_seg(a, blk);
+  const int64_t shard_off = a.seg[s].shard_off;
+  const int64_t full_off = a.seg[s].full_off;
+  const int64_t dst_off = a.seg[s].dst_off;
+  const uint32_t len = (uint32_t)a.seg[s].len;
+  const uint32_t e = (uint32_t)(blk - a.seg[s].block_start) * kThreads + threadIdx.x;
+  if (e >= len) return;
+
+  float g;
+  if constexpr (MODE == kFromReduced) {
+    g = gaddr<const gf32*>(a.reduced)[shard_off + e];
+  } else {
+    const int n = a.n_ranks;
+    float acc;
+    int q = 0;
+    if (MODE == kReduceOnly && (a.flags & kFlagInitFromOut)) {
+      acc = gaddr<const gf32*>(a.out)[shard_off + e];
+    } else {
+      acc = widen1<GDT>(gaddr<const gu16*>(rank_base(a, 0, shard_off, full_off))[e]);
+      q = 1;
+    }
+    for (; q < n; ++q)
+      acc = acc + widen1<GDT>(gaddr<const gu16*>(rank_base(a, q, shard_off, full_off))[e]);
+    if (MODE == kReduceOnly) {
+      if (a.flags & kFlagApplyScale) acc = acc * a.c[8];
+      gaddr<gf32*>(a.out)[shard_off + e] = acc;
+      return;
+    }
+    g = acc * a.c[8];
+  }
+  if constexpr (MODE != kReduceOnly) {
+    const AdamC k = load_consts(a);
+    gf32* wp = gaddr<gf32*>(a.master);
+    gf32* mp = gaddr<gf32*>(a.m);
+    gf32* vp = gaddr<gf32*>(a.v);
+    float w = wp[shard_off + e], m = mp[shard_off + e], v = vp[shard_off + e];
+    adam1(k, g, w, m, v);
+    wp[shard_off + e] = w;
+    mp[shard_off + e] = m;
+    vp[shard_off + e] = v;
+    gaddr<gu16*>(a.dst)[dst_off + e] = (uint16_t)narrow1<PDT>(w);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Copies (flatten, gather_pack)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int find_ent(const CopyArgs& a, int blk) {
+  int lo = 0, hi = a.n_ent - 1;   // last entry whose block_start <= blk
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.ent[mid].block_start <= blk) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// The 16 bytes that start kb bytes (0..3) into dword j0 (0..3) of the
+// 32-byte window lo:hi.
+__device__ __forceinline__ u32x4 funnel(const u32x4 lo, const u32x4 hi, int j0, uint32_t kb) {
+  const uint32_t d[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  u32x4 r;
+  switch (j0) {
+    case 0:
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_alignbyte(d[i + 1], d[i], kb);
+      break;
+    case 1:
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_alignbyte(d[i + 2], d[i + 1], kb);
+      break;
+    case 2:
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_alignbyte(d[i + 3], d[i + 2], kb);
+      break;
+    default:
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_alignbyte(d[i + 4], d[i + 3], kb);
+      break;
+  }
+  return r;
+}
+
+template <int ESZ>
+struct ElemT;
+template <>
+struct ElemT<2> { typedef gu16 T; };
+template <>
+struct ElemT<4> { typedef gu32 T; };
+
+template <int ESZ>
+__global__ void __launch_bounds__(kThreads) copy_kernel(const CopyArgs a) {
+  typedef typename ElemT<ESZ>::T T;
+  const int blk = blockIdx.x;
+  const int ei = find_ent(a, blk);
+  const uint64_t s_begin = (uint64_t)(uintptr_t)a.ent[ei].src;
+  const bool zero_fill = s_begin == 0;
+  const int64_t n = a.ent[ei].n;
+  // The entry's destination bytes [d0, d1) and its 16-byte units.
+  const uint64_t d0 = (uint64_t)(uintptr_t)a.dst + (uint64_t)a.ent[ei].dst_off * ESZ;
+  const uint64_t d1 = d0 + (uint64_t)n * ESZ;
+  const uint64_t u_end = (d1 + 15) >> 4;
+  const uint64_t ublk =
+      (d0 >> 4) + (uint64_t)(blk - a.ent[ei].block_start) * (kThreads * kCopyUnits);
+  const uint64_t s_end = s_begin + (uint64_t)n * ESZ;
+  const uint64_t shift = s_begin - d0;   // source byte = destination byte + shift (mod 2^64)
+#pragma unroll
+  for (int i = 0; i < kCopyUnits; ++i) {
+    const uint64_t u = ublk + (uint64_t)i * kThreads + threadIdx.x;
+    if (u >= u_end) break;
+    const uint64_t ub = u << 4;
+    const uint64_t lo = ub > d0 ? ub : d0;
+    const uint64_t hi = ub + 16 < d1 ? ub + 16 : d1;
+    bool done = false;
+    if (lo == ub && hi == ub + 16) {
+      gu32x4* const up = gaddr<gu32x4*>(ub);
+      if (zero_fill) {
+        st_nt(up, u32x4{0u, 0u, 0u, 0u});
+        done = true;
+      } else {
+        const uint64_t p = ub + shift;
+        const uint32_t k = (uint32_t)(p & 15);
+        if (k == 0) {
+          st_nt(up, ld_nt(gaddr<const gu32x4*>(p)));
+          done = true;
+        } else {
+          const uint64_t A = p - k;
+          if (A >= s_begin && A + 32 <= s_end) {   // both aligned loads inside the source
+            const u32x4 w0 = ld_nt(gaddr<const gu32x4*>(A));
+            const u32x4 w1 = ld_nt(gaddr<const gu32x4*>(A + 16));
+            st_nt(up, funnel(w0, w1, (int)(k >> 2), k & 3u));
+            done = true;
+          }
+        }
+      }
+    }
+    if (!done) {
+      for (uint64_t b = lo; b < hi; b += ESZ) {
+        *gaddr<T*>(b) = zero_fill ? 0 : *gaddr<const T*>(b + shift);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch
+// ---------------------------------------------------------------------------
+
+template <int MODE, int GDT, int PDT>
+void* pick_ndc(int ndc) {
+  switch (ndc) {
+    case 4: return (void*)&step_vec_kernel<MODE, GDT, PDT, 4>;
+    case 8: return (void*)&step_vec_kernel<MODE, GDT, PDT, 8>;
+    case 16: return (void*)&step_vec_kernel<MODE, GDT, PDT, 16>;
+    case 64: return (void*)&step_vec_kernel<MODE, GDT, PDT, 64>;
+    default: return (void*)&step_vec_kernel<MODE, GDT, PDT, 0>;
+  }
+}
+
+template <int MODE, int GDT, int PDT>
+void* pick_step(int ndc, bool vec) {
+  if (!vec) return (void*)&step_elem_kernel<MODE, GDT, PDT>;
+  return pick_ndc<MODE, GDT, PDT>(ndc);
+}
+
+void* pick_kernel(int mode, int gdt, int pdt, int ndc, bool vec) {
+  const bool gb = gdt == ZERO_BF16, pb = pdt == ZERO_BF16;
+  if (mode == kFromReduced) {   // gradient type and rank count play no part
+    if (pb) return vec ? (void*)&step_vec_kernel<kFromReduced, ZERO_BF16, ZERO_BF16, 1>
+                       : (void*)&step_elem_kernel<kFromReduced, ZERO_BF16, ZERO_BF16>;
+    return vec ? (void*)&step_vec_kernel<kFromReduced, ZERO_BF16, ZERO_F16, 1>
+               : (void*)&step_elem_kernel<kFromReduced, ZERO_BF16, ZERO_F16>;
+  }
+  if (mode == kReduceOnly) {    // parameter type plays no part
+    return gb ? pick_step<kReduceOnly, ZERO_BF16, ZERO_F16>(ndc, vec)
+              : pick_step<kReduceOnly, ZERO_F16, ZERO_F16>(ndc, vec);
+  }
+  if (gb && pb) return pick_step<kFused, ZERO_BF16, ZERO_BF16>(ndc, vec);
+  if (gb) return pick_step<kFused, ZERO_BF16, ZERO_F16>(ndc, vec);
+  if (pb) return pick_step<kFused, ZERO_F16, ZERO_BF16>(ndc, vec);
+  return pick_step<kFused, ZERO_F16, ZERO_F16>(ndc, vec);
+}
+
+}  // namespace
+
+int launch_step(const StepArgs& a, int mode, int gdt, int pdt, int ndc, bool vec, int n_blocks,
+                void* stream) {
+  void* fn = pick_kernel(mode, gdt, pdt, ndc, vec);
+  void* args[] = {(void*)&a};
+  return (int)hipLaunchKernel(fn, dim3((unsigned)n_blocks), dim3(kThreads), args, 0,
+                              (hipStream_t)stream);
+}
+
+int launch_copy(const CopyArgs& a, int esz, int n_blocks, void* stream) {
+  void* fn = esz == 2 ? (void*)&copy_kernel<2> : (void*)&copy_kernel<4>;
+  void* args[] = {(void*)&a};
+  return (int)hipLaunchKernel(fn, dim3((unsigned)n_blocks), dim3(kThreads), args, 0,
+                              (hipStream_t)stream);
+}
+
+const char* hip_error_string(int err) { return hipGetErrorString((hipError_t)err); }
+
+}  // namespace zk
