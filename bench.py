@@ -78,13 +78,27 @@ def cpu_baseline(cfg, n_sample: int):
                       f"{DTYPE_NAME[cfg.gdt]} slices, one step (t={t_check}); {dt:.2f} s"}
 
 
+def copy_probe(torch):
+    """A plain device copy of known size, for scaling rocprofv3's FETCH_SIZE and
+    WRITE_SIZE counters to bytes: each dispatch reads and writes 4 GiB."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": "copy", "bytes_read_per_dispatch": 4 * n, "bytes_written_per_dispatch": 4 * n}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3)
-    ap.add_argument("--cpu-sample", type=int, default=1 << 22)
+    ap.add_argument("--cpu-sample", type=int, default=1 << 24)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="time a plain 4 GiB device copy (calibrates HBM byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -94,6 +108,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_probe:
+        copy_probe(torch)
+        return
     from synth.workloads import CONFIGS, GpuRun
     from __graft_entry__ import _ensure_built
     _ensure_built()

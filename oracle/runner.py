@@ -38,17 +38,15 @@ class OracleRun:
     def rank_positions(self, rank: int, sample=None):
         """Flat positions of rank's shard (shard-local order), and pad flags,
         from the oracle plan's owned ranges."""
-        parts, pads = [], []
-        for b, bk in enumerate(self.plan.buckets):
-            lo, hi = self.plan.owner_range(b, rank)
-            pos = np.arange(lo, hi, dtype=np.int64)
-            parts.append(pos)
-            pads.append(pos >= bk.flat_off + bk.numel)
-        pos = np.concatenate(parts) if parts else np.zeros(0, np.int64)
-        pad = np.concatenate(pads) if pads else np.zeros(0, bool)
-        if sample is not None:
-            pos, pad = pos[sample], pad[sample]
-        return pos, pad
+        j = np.arange(self.plan.shard_total, dtype=np.int64) if sample is None else sample
+        if not self.plan.buckets:
+            return j.copy(), np.zeros(j.size, bool)
+        starts = np.array([bk.shard_off for bk in self.plan.buckets], dtype=np.int64)
+        b = np.searchsorted(starts, j, side="right") - 1          # bucket of each shard index
+        lo = np.array([self.plan.owner_range(i, rank)[0] for i in range(len(starts))], np.int64)
+        real_end = np.array([bk.flat_off + bk.numel for bk in self.plan.buckets], np.int64)
+        pos = lo[b] + (j - starts[b])
+        return pos, pos >= real_end[b]
 
     def initial_param_shard(self, q: int, layer: int) -> np.ndarray:
         pos, pad = self.rank_positions(q)

@@ -3,9 +3,10 @@
 This module holds no arithmetic of the ZeRO step.  It only defines which
 numbers sit at which position of which buffer, so that the CPU oracle and the
 GPU library can be fed identical bytes without either producing the other's
-inputs.  The same definition is implemented twice: here with numpy (for the
-oracle, and for sampled positions of full-size workloads) and in
-``synth_fill.hip`` (bulk fills on the GPU).  Tests check the two bit for bit.
+inputs.  The same definition is implemented three times: with numpy here
+(the readable reference, ``*_np``), in ``synth_cpu.c`` (the fast host path the
+oracle side uses) and in ``synth_fill.hip`` (bulk fills on the GPU).  Tests
+check them against each other bit for bit.
 
 Definition
 ----------
@@ -99,13 +100,13 @@ def irwin_hall_int(u: np.ndarray) -> np.ndarray:
     return s.astype(np.int64) - 131070
 
 
-def normal_f32(key: int, positions: np.ndarray, sigma: float) -> np.ndarray:
+def normal_f32_np(key: int, positions: np.ndarray, sigma: float) -> np.ndarray:
     s = irwin_hall_int(draw_u64(key, positions)).astype(np.float32)
     return (s * scale_for(sigma)).astype(np.float32)
 
 
-def mix_f32(key: int, sel_key: int, positions: np.ndarray, sigma: float) -> np.ndarray:
-    x = normal_f32(key, positions, sigma)
+def mix_f32_np(key: int, sel_key: int, positions: np.ndarray, sigma: float) -> np.ndarray:
+    x = normal_f32_np(key, positions, sigma)
     w = draw_u64(sel_key, positions)
     hi = w >> np.uint64(32)
     zero = hi < np.uint64(ZERO_CUT)
@@ -114,6 +115,44 @@ def mix_f32(key: int, sel_key: int, positions: np.ndarray, sigma: float) -> np.n
     x = np.where(zero, np.float32(0.0), x)
     x = np.where(outl, sign, x).astype(np.float32)
     return x
+
+
+_cpu_lib = None
+
+
+def _cpu():
+    """The C implementation of the same definition (synth_cpu.c), for speed."""
+    global _cpu_lib
+    if _cpu_lib is None:
+        import ctypes
+        import os
+        from . import _build
+        if not os.path.exists(_build.CPU_LIB):
+            _build.build_cpu()
+        L = ctypes.CDLL(_build.CPU_LIB)
+        L.synth_values_f32.restype = None
+        L.synth_values_f32.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint64,
+                                       ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_float]
+        _cpu_lib = L
+    return _cpu_lib
+
+
+def values_f32_c(key: int, sel_key: int, mix: bool, positions: np.ndarray, sigma: float) -> np.ndarray:
+    import ctypes
+    pos = np.ascontiguousarray(positions, dtype=np.int64)
+    out = np.empty(pos.size, dtype=np.float32)
+    _cpu().synth_values_f32(ctypes.c_void_p(out.ctypes.data), pos.size, key & M64, sel_key & M64,
+                            1 if mix else 0, ctypes.c_void_p(pos.ctypes.data), 0,
+                            ctypes.c_float(float(scale_for(sigma))))
+    return out
+
+
+def normal_f32(key: int, positions: np.ndarray, sigma: float) -> np.ndarray:
+    return values_f32_c(key, 0, False, positions, sigma)
+
+
+def mix_f32(key: int, sel_key: int, positions: np.ndarray, sigma: float) -> np.ndarray:
+    return values_f32_c(key, sel_key, True, positions, sigma)
 
 
 def to_dtype_bits(x: np.ndarray, dt: int) -> np.ndarray:
@@ -138,8 +177,8 @@ def grad_values(seed: int, rank: int, step: int, positions: np.ndarray, sigma: f
         x = mix_f32(k, key_of(seed, STREAM_MIXSEL, rank, step), positions, sigma)
     else:
         x = normal_f32(k, positions, sigma)
-    if pad_mask is not None:
-        x = np.where(pad_mask, np.float32(0.0), x).astype(np.float32)
+    if pad_mask is not None and pad_mask.any():
+        x[pad_mask] = np.float32(0.0)
     return to_dtype_bits(x, dt)
 
 
@@ -147,6 +186,6 @@ def master_values(seed: int, positions: np.ndarray, sigma: float,
                   pad_mask: np.ndarray | None = None) -> np.ndarray:
     k = key_of(seed, STREAM_MASTER, 0, 0)
     x = normal_f32(k, positions, sigma)
-    if pad_mask is not None:
-        x = np.where(pad_mask, np.float32(0.0), x).astype(np.float32)
+    if pad_mask is not None and pad_mask.any():
+        x[pad_mask] = np.float32(0.0)
     return x

@@ -15,6 +15,7 @@ def load():
     if _lib is None:
         if not os.path.exists(_build.LIB):
             raise ImportError(f"libsynth.so not built at {_build.LIB}")
+        import torch  # noqa: F401  -- bind to torch's HIP runtime (see zero_sharded_mixed_02_amd.load)
         L = ctypes.CDLL(_build.LIB)
         L.synth_fill.restype = ctypes.c_int
         L.synth_fill.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64,

@@ -203,3 +203,17 @@ def test_binding_without_library_fails_loudly(tmp_path, monkeypatch):
     with pytest.raises(ImportError):
         Z.load()
     importlib.reload(Z)
+
+
+def test_single_hip_runtime_in_process():
+    """libzero.so and libsynth.so must bind to the HIP runtime torch loaded,
+    whichever is opened first (two runtimes in one process see no device)."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import zero_sharded_mixed_02_amd as Z; Z.load()\n"
+            "from synth import gpu; gpu.load()\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n") % ROOT
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True)
+    assert out.stdout.strip() == "1"

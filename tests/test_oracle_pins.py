@@ -163,6 +163,26 @@ def test_plan_bruteforce_invariants(oracle_lib):
         assert np.array_equal(O.gather_pack(p, shards), flat)
 
 
+def test_runner_positions_match_shard_of(oracle_lib):
+    """The oracle driver's index -> flat position map is the plan's ownership
+    rule: it equals shard_of applied to the identity, and flags exactly the
+    padding."""
+    from dataclasses import replace
+    from oracle.runner import OracleRun
+    from synth.workloads import Config
+    O = oracle_lib
+    for n_d, align, sizes, cap in _random_plans(31, 80):
+        if not sizes:
+            continue
+        cfg = Config("t", tuple(sizes), n_d=n_d, gdt=O.BF16, pdt=O.F16, bucket_cap=cap, align=align)
+        for rank in range(n_d):
+            run = OracleRun(replace(cfg, owner=rank))
+            p = run.plan
+            ident = np.arange(p.psi_pad, dtype=np.int64)
+            assert np.array_equal(run.pos, O.shard_of(p, rank, ident))
+            assert np.array_equal(run.pad, np.array([p.is_pad(int(x)) for x in run.pos], bool))
+
+
 def test_plan_rejects_bad_arguments(oracle_lib):
     O = oracle_lib
     with pytest.raises(ValueError):

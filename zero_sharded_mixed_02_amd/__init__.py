@@ -52,6 +52,18 @@ class _GradSrc(ctypes.Structure):
 _lib = None
 
 
+def _share_torch_hip_runtime():
+    """PyTorch brings its own copy of the HIP runtime (same soname as
+    /opt/rocm's).  Device memory and streams come from torch, so libzero.so
+    must bind to that same runtime: loading torch first makes the dynamic
+    loader resolve libzero's libamdhip64.so.7 to torch's already-loaded copy
+    instead of opening a second runtime in the process."""
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+
+
 def load():
     """Load libzero.so.  Raises if it has not been built."""
     global _lib
@@ -59,6 +71,7 @@ def load():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libzero.so not built at {LIB_PATH}; run __graft_entry__.build()")
+    _share_torch_hip_runtime()
     L = ctypes.CDLL(LIB_PATH)
     i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
     p_i64, p_i32 = ctypes.POINTER(i64), ctypes.POINTER(i32)

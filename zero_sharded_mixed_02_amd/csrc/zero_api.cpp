@@ -121,7 +121,7 @@ int ndc_for(int n) { return (n == 4 || n == 8 || n == 16 || n == 64) ? n : 0; }
 // Launch the step kernel over all pieces, in chunks of kMaxSeg.
 zero_status run_step(zk::StepArgs& a, const std::vector<Piece>& ps, int mode, int gdt, int pdt,
                      bool vec, void* stream) {
-  const int per_block = zk::kThreads * (vec ? zk::kStepVec : 1);
+  const int per_block = vec ? zk::kStepThreads * zk::kStepVec : zk::kThreads;
   size_t i = 0;
   while (i < ps.size()) {
     int nseg = 0;

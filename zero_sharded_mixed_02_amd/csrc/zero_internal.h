@@ -16,7 +16,8 @@ constexpr int kMaxSeg = 64;                  // shard segments per step launch
 constexpr int kMaxCopy = 112;                // copy entries per copy launch
 constexpr int64_t kSegMaxElems = int64_t(1) << 28;  // keeps per-lane byte offsets in 32 bits
 
-constexpr int kThreads = 256;               // 4 wave64s per workgroup
+constexpr int kThreads = 256;               // copy and element kernels: 4 wave64s
+constexpr int kStepThreads = 512;           // vector step kernel: 8 wave64s (8 wave tiles)
 constexpr int kStepVec = 8;                 // elements per lane in the vector step kernel
 constexpr int kCopyUnits = 4;               // 16-byte units per lane in the copy kernel
 

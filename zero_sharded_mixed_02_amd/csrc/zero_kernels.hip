@@ -8,11 +8,12 @@
 //    arithmetic of reduce-scatter), then run the mixed-precision Adam update on
 //    the fp32 master weight and moments and store the rounded 16-bit parameter
 //    into the all-gather buffer -- all in registers, one HBM pass.  In the
-//    vector kernel each lane owns 8 consecutive elements: one 16-byte load per
-//    rank, two per fp32 state array, one 16-byte parameter store.  Every rank
-//    pointer and segment offset is wave-uniform, so address arithmetic stays on
-//    the scalar unit and vector accesses are an SGPR base plus a 32-bit lane
-//    offset.
+//    vector kernel each lane owns two groups of 4 elements laid out so that
+//    every wave-wide load or store covers whole contiguous 128-byte lines:
+//    per rank two 8-byte loads, per fp32 state array two 16-byte loads and
+//    stores, two 8-byte parameter stores.  Every rank pointer and segment
+//    offset is wave-uniform, so address arithmetic stays on the scalar unit
+//    and vector accesses are an SGPR base plus a 32-bit lane offset.
 //
 //  * copy kernel: destination-aligned 16-byte copies used by flatten (ragged
 //    tensors into padded buckets, at any element offset) and gather_pack
@@ -34,9 +35,11 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // Global-address-space views, so that accesses are global_* (not flat_*).
 typedef __attribute__((address_space(1))) u32x4 gu32x4;
 typedef __attribute__((address_space(1))) f32x4 gf32x4;
+typedef __attribute__((address_space(1))) u32x2 gu32x2;
 typedef __attribute__((address_space(1))) uint16_t gu16;
 typedef __attribute__((address_space(1))) uint32_t gu32;
 typedef __attribute__((address_space(1))) float gf32;
@@ -53,26 +56,13 @@ __device__ __forceinline__ T gaddr(uint64_t p) {
 // Streaming (non-temporal) accesses: every byte of the step is touched once.
 __device__ __forceinline__ u32x4 ld_nt(const gu32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ f32x4 ld_nt(const gf32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ u32x2 ld_nt(const gu32x2* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st_nt(gu32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void st_nt(gu32x2* p, u32x2 v) { __builtin_nontemporal_store(v, p); }
 __device__ __forceinline__ void st_nt(gf32x4* p, f32x4 v) { __builtin_nontemporal_store(v, p); }
 
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-}
-
-// 8 packed 16-bit values -> 8 fp32 values (exact widening).
-template <int GDT>
-__device__ __forceinline__ void widen8(const u32x4 r, float (&x)[8]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if constexpr (GDT == ZERO_BF16) {
-      x[2 * i] = __uint_as_float(r[i] << 16);
-      x[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
-    } else {
-      x[2 * i] = f16_bits_to_f32(r[i] & 0xffffu);
-      x[2 * i + 1] = f16_bits_to_f32(r[i] >> 16);
-    }
-  }
 }
 
 template <int GDT>
@@ -130,146 +120,171 @@ __device__ __forceinline__ uint64_t rank_base(const StepArgs& a, int q, int64_t 
   return (uint64_t)(uintptr_t)a.grad[q] + (uint64_t)((full ? full_off : shard_off) * 2);
 }
 
-__device__ __forceinline__ const gu32x4* grad_vec(const StepArgs& a, int q, int64_t shard_off,
-                                                  int64_t full_off, uint32_t boff) {
-  return gaddr<const gu32x4*>(rank_base(a, q, shard_off, full_off)) + (boff >> 4);
+// Lane -> element mapping of the vector kernel.  A wave owns a tile of 512
+// consecutive elements; lane l owns two groups of 4: elements [4l, 4l+4) and
+// [256+4l, 256+4l+4) of the tile.  Every memory instruction of the wave then
+// covers one contiguous span -- 512 bytes of a 16-bit array, 1 KiB of an fp32
+// array -- made of whole 128-byte lines, so no line is fetched or written
+// back in halves by two different instructions.
+constexpr uint32_t kTile = 512;
+constexpr uint32_t kHalf = 256;
+
+__device__ __forceinline__ const gu32x2* grad_pair(const StepArgs& a, int q, int64_t shard_off,
+                                                   int64_t full_off, uint32_t boff) {
+  return gaddr<const gu32x2*>(rank_base(a, q, shard_off, full_off)) + (boff >> 3);
 }
 
-// Fold the launch's ranks for 8 consecutive elements at byte offset boff of
-// each rank's segment base.  CONT = false: the fold starts from rank 0's value;
+// 4 packed 16-bit values -> 4 fp32 values (exact widening).
+template <int GDT>
+__device__ __forceinline__ void widen4(const u32x2 r, float* x) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if constexpr (GDT == ZERO_BF16) {
+      x[2 * i] = __uint_as_float(r[i] << 16);
+      x[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+    } else {
+      x[2 * i] = f16_bits_to_f32(r[i] & 0xffffu);
+      x[2 * i + 1] = f16_bits_to_f32(r[i] >> 16);
+    }
+  }
+}
+
+// Fold the launch's ranks for the lane's two 4-element groups (byte offsets
+// boa, bob of each rank's segment base).  acc[0..3] is group a, acc[4..7]
+// group b.  CONT = false: the fold starts from the first rank's value;
 // CONT = true: every rank is added to the incoming acc (continuing a fold
 // begun by an earlier launch).  Loads are issued in batches of B ranks ahead
-// of their adds so that B KiB per wave are in flight; adds keep rank order.
+// of their adds, so B KiB per wave are in flight; adds keep rank order.
 template <int GDT, int NDC, bool CONT>
-__device__ __forceinline__ void fold8(const StepArgs& a, int64_t shard_off, int64_t full_off,
-                                      uint32_t boff, float (&acc)[8]) {
+__device__ __forceinline__ void fold(const StepArgs& a, int64_t shard_off, int64_t full_off,
+                                     uint32_t boa, uint32_t bob, float (&acc)[8]) {
+  auto take = [&](const u32x2 ra, const u32x2 rb, bool first) {
+    float x[8];
+    widen4<GDT>(ra, x);
+    widen4<GDT>(rb, x + 4);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = first ? x[k] : acc[k] + x[k];
+  };
   if constexpr (NDC > 0) {
     constexpr int B = NDC < 16 ? NDC : 16;
 #pragma unroll
     for (int q0 = 0; q0 < NDC; q0 += B) {
-      u32x4 raw[B];
-#pragma unroll
-      for (int i = 0; i < B; ++i) raw[i] = ld_nt(grad_vec(a, q0 + i, shard_off, full_off, boff));
+      u32x2 ra[B], rb[B];
 #pragma unroll
       for (int i = 0; i < B; ++i) {
-        float x[8];
-        widen8<GDT>(raw[i], x);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[k] = (!CONT && q0 + i == 0) ? x[k] : acc[k] + x[k];
+        ra[i] = ld_nt(grad_pair(a, q0 + i, shard_off, full_off, boa));
+        rb[i] = ld_nt(grad_pair(a, q0 + i, shard_off, full_off, bob));
       }
+#pragma unroll
+      for (int i = 0; i < B; ++i) take(ra[i], rb[i], !CONT && q0 + i == 0);
     }
   } else {
     const int n = a.n_ranks;
     int q = 0;
     if (!CONT) {
-      float x[8];
-      widen8<GDT>(ld_nt(grad_vec(a, 0, shard_off, full_off, boff)), x);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] = x[k];
+      take(ld_nt(grad_pair(a, 0, shard_off, full_off, boa)),
+           ld_nt(grad_pair(a, 0, shard_off, full_off, bob)), true);
       q = 1;
     }
     constexpr int B = 8;
     for (; q + B <= n; q += B) {
-      u32x4 raw[B];
-#pragma unroll
-      for (int i = 0; i < B; ++i) raw[i] = ld_nt(grad_vec(a, q + i, shard_off, full_off, boff));
+      u32x2 ra[B], rb[B];
 #pragma unroll
       for (int i = 0; i < B; ++i) {
-        float x[8];
-        widen8<GDT>(raw[i], x);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[k] = acc[k] + x[k];
+        ra[i] = ld_nt(grad_pair(a, q + i, shard_off, full_off, boa));
+        rb[i] = ld_nt(grad_pair(a, q + i, shard_off, full_off, bob));
       }
-    }
-    for (; q < n; ++q) {
-      float x[8];
-      widen8<GDT>(ld_nt(grad_vec(a, q, shard_off, full_off, boff)), x);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] = acc[k] + x[k];
+      for (int i = 0; i < B; ++i) take(ra[i], rb[i], false);
     }
+    for (; q < n; ++q)
+      take(ld_nt(grad_pair(a, q, shard_off, full_off, boa)),
+           ld_nt(grad_pair(a, q, shard_off, full_off, bob)), false);
   }
 }
 
-__device__ __forceinline__ void load8(const gf32x4* p, float (&x)[8]) {
-  const f32x4 a = ld_nt(p), b = ld_nt(p + 1);
+// fp32 groups: x[0..3] at element ea, x[4..7] at element eb of array base p.
+__device__ __forceinline__ void load_groups(const float* p, uint32_t ea, uint32_t eb, float (&x)[8]) {
+  const f32x4 u = ld_nt(gaddr<const gf32x4*>(p) + (ea >> 2));
+  const f32x4 w = ld_nt(gaddr<const gf32x4*>(p) + (eb >> 2));
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    x[k] = a[k];
-    x[4 + k] = b[k];
+    x[k] = u[k];
+    x[4 + k] = w[k];
   }
 }
 
-__device__ __forceinline__ void store8(gf32x4* p, const float (&x)[8]) {
-  f32x4 a, b;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    a[k] = x[k];
-    b[k] = x[4 + k];
-  }
-  st_nt(p, a);
-  st_nt(p + 1, b);
+__device__ __forceinline__ void store_groups(float* p, uint32_t ea, uint32_t eb, bool vb,
+                                             const float (&x)[8]) {
+  st_nt(gaddr<gf32x4*>(p) + (ea >> 2), f32x4{x[0], x[1], x[2], x[3]});
+  if (vb) st_nt(gaddr<gf32x4*>(p) + (eb >> 2), f32x4{x[4], x[5], x[6], x[7]});
 }
 
-// Vector kernel: 8 elements per lane.  The host takes this kernel only when
-// every segment offset and length is a multiple of 8 elements and every base
-// address is 16-byte aligned.
+// Vector kernel.  The host takes it only when every segment offset and length
+// is a multiple of 8 elements and every base address is 16-byte aligned; a
+// segment's last wave tile may be partial, in which case a lane's second group
+// can lie past the end: its loads then repeat the first group's addresses
+// (in bounds) and its stores are skipped.
 template <int MODE, int GDT, int PDT, int NDC>
-__global__ void __launch_bounds__(kThreads) step_vec_kernel(const StepArgs a) {
+__global__ void __launch_bounds__(kStepThreads) step_vec_kernel(const StepArgs a) {
   const int blk = blockIdx.x;
   const int s = find_seg(a, blk);
   const int64_t shard_off = a.seg[s].shard_off;
   const int64_t full_off = a.seg[s].full_off;
   const int64_t dst_off = a.seg[s].dst_off;
   const uint32_t len = (uint32_t)a.seg[s].len;
-  const uint32_t e = (uint32_t)(blk - a.seg[s].block_start) * (kThreads * kStepVec) +
-                     threadIdx.x * kStepVec;
-  if (e >= len) return;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t tile = (uint32_t)(blk - a.seg[s].block_start) * (kStepThreads * kStepVec) +
+                        (threadIdx.x >> 6) * kTile;
+  const uint32_t ea = tile + 4u * lane;
+  if (ea >= len) return;
+  const bool vb = ea + kHalf < len;
+  const uint32_t eb = vb ? ea + kHalf : ea;
 
   float g[8];
   if constexpr (MODE == kFromReduced) {
-    load8(gaddr<const gf32x4*>(a.reduced + shard_off) + (e >> 2), g);
+    load_groups(a.reduced + shard_off, ea, eb, g);
   } else if constexpr (MODE == kFused) {
     float acc[8];
-    fold8<GDT, NDC, false>(a, shard_off, full_off, e * 2u, acc);
+    fold<GDT, NDC, false>(a, shard_off, full_off, ea * 2u, eb * 2u, acc);
     const float gs = a.c[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) g[k] = acc[k] * gs;
   } else {  // kReduceOnly
-    gf32x4* op = gaddr<gf32x4*>(a.out + shard_off) + (e >> 2);
     float acc[8];
     if (a.flags & kFlagInitFromOut) {
       // The fp32 prefix of the fold was stored exactly by the previous launch.
-      load8(op, acc);
-      fold8<GDT, NDC, true>(a, shard_off, full_off, e * 2u, acc);
+      load_groups(a.out + shard_off, ea, eb, acc);
+      fold<GDT, NDC, true>(a, shard_off, full_off, ea * 2u, eb * 2u, acc);
     } else {
-      fold8<GDT, NDC, false>(a, shard_off, full_off, e * 2u, acc);
+      fold<GDT, NDC, false>(a, shard_off, full_off, ea * 2u, eb * 2u, acc);
     }
     if (a.flags & kFlagApplyScale) {
       const float gs = a.c[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[k] = acc[k] * gs;
     }
-    store8(op, acc);
+    store_groups(a.out + shard_off, ea, eb, vb, acc);
   }
 
   if constexpr (MODE != kReduceOnly) {
     const AdamC k = load_consts(a);
-    gf32x4* wp = gaddr<gf32x4*>(a.master + shard_off) + (e >> 2);
-    gf32x4* mp = gaddr<gf32x4*>(a.m + shard_off) + (e >> 2);
-    gf32x4* vp = gaddr<gf32x4*>(a.v + shard_off) + (e >> 2);
     float w[8], m[8], v[8];
-    load8(wp, w);
-    load8(mp, m);
-    load8(vp, v);
+    load_groups(a.master + shard_off, ea, eb, w);
+    load_groups(a.m + shard_off, ea, eb, m);
+    load_groups(a.v + shard_off, ea, eb, v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) adam1(k, g[i], w[i], m[i], v[i]);
-    u32x4 p;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = narrow1<PDT>(w[2 * i]) | (narrow1<PDT>(w[2 * i + 1]) << 16);
-    store8(wp, w);
-    store8(mp, m);
-    store8(vp, v);
-    st_nt(gaddr<gu32x4*>((uint16_t*)a.dst + dst_off) + (e >> 3), p);
+    store_groups(a.master + shard_off, ea, eb, vb, w);
+    store_groups(a.m + shard_off, ea, eb, vb, m);
+    store_groups(a.v + shard_off, ea, eb, vb, v);
+    const u32x2 pa = {narrow1<PDT>(w[0]) | (narrow1<PDT>(w[1]) << 16),
+                      narrow1<PDT>(w[2]) | (narrow1<PDT>(w[3]) << 16)};
+    const u32x2 pb = {narrow1<PDT>(w[4]) | (narrow1<PDT>(w[5]) << 16),
+                      narrow1<PDT>(w[6]) | (narrow1<PDT>(w[7]) << 16)};
+    gu32x2* const dp = gaddr<gu32x2*>((uint16_t*)a.dst + dst_off);
+    st_nt(dp + (ea >> 2), pa);
+    if (vb) st_nt(dp + (eb >> 2), pb);
   }
 }
 
@@ -469,8 +484,8 @@ int launch_step(const StepArgs& a, int mode, int gdt, int pdt, int ndc, bool vec
                 void* stream) {
   void* fn = pick_kernel(mode, gdt, pdt, ndc, vec);
   void* args[] = {(void*)&a};
-  return (int)hipLaunchKernel(fn, dim3((unsigned)n_blocks), dim3(kThreads), args, 0,
-                              (hipStream_t)stream);
+  return (int)hipLaunchKernel(fn, dim3((unsigned)n_blocks), dim3(vec ? kStepThreads : kThreads), args,
+                              0, (hipStream_t)stream);
 }
 
 int launch_copy(const CopyArgs& a, int esz, int n_blocks, void* stream) {
