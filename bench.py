@@ -78,6 +78,150 @@ def cpu_baseline(cfg, n_sample: int):
                       f"{DTYPE_NAME[cfg.gdt]} slices, one step (t={t_check}); {dt:.2f} s"}
 
 
+def _time_launches(torch, fn, reps=20, warmup=3):
+    """Average milliseconds per call of fn (one or more launches on torch's
+    current stream), from HIP events around each call."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    st = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    en = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        st[i].record(stream)
+        fn()
+        en[i].record(stream)
+    torch.cuda.synchronize()
+    return sum(s.elapsed_time(e) for s, e in zip(st, en)) / reps
+
+
+def _entry(ms, nbytes, elems):
+    gbps = nbytes / (ms / 1e3) / 1e9
+    return {"ms": ms, "algorithmic_bytes": nbytes, "gbps": gbps, "frac_hbm_peak": gbps / HBM_PEAK_GBPS,
+            "elements_per_s": elems / (ms / 1e3)}
+
+
+def measure_kernels(torch):
+    """Every entry point at its own workload (see the design doc for the byte
+    counts): fused step on the 7.5B, 13B and GPT-2 workloads, the unfused
+    reduce and Adam-from-reduced on 7.5B, flatten of the GPT-2 tensor list,
+    and the Stage-3 layer (gather_pack, then fused step)."""
+    import zero_sharded_mixed_02_amd as Z
+    import synth
+    from synth import gpu as SG
+    from synth.workloads import CONFIGS, GpuRun, gpt2_small_sizes
+    out = {}
+
+    def free():
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+    # 7.5B, N_d = 64: fused, and the two unfused halves.
+    cfg = CONFIGS[3]
+    run = GpuRun(cfg)
+    S = run.S
+    run.fill_grads(1)
+    t = [0]
+
+    def fused():
+        t[0] += 1
+        run.step(t[0])
+    out["fused_7.5B_nd64"] = _entry(_time_launches(torch, fused), (2 * 64 + 26) * S, S)
+    red = torch.empty(S, dtype=torch.float32, device="cuda")
+    out["reduce_7.5B_nd64"] = _entry(_time_launches(torch, lambda: run.reduce(red)), (2 * 64 + 4) * S, S)
+
+    def from_reduced():
+        t[0] += 1
+        run.step_from_reduced(t[0], red)
+    out["adam_from_reduced_7.5B"] = _entry(_time_launches(torch, from_reduced), (4 + 24 + 2) * S, S)
+    del red, run
+    free()
+    log("7.5B kernels done")
+
+    # 13B Stage 1, N_d = 16 (owner's full buffer + 15 owned slices).
+    run = GpuRun(CONFIGS[4])
+    S = run.S
+    run.fill_grads(1)
+    out["fused_13B_stage1_nd16"] = _entry(_time_launches(torch, fused, reps=10), (2 * 16 + 26) * S, S)
+    del run
+    free()
+    log("13B kernels done")
+
+    # GPT-2-small list, N_d = 8, 7 buckets (partly cache-resident).
+    run = GpuRun(CONFIGS[2])
+    S = run.S
+    run.fill_grads(1)
+    out["fused_gpt2_nd8"] = _entry(_time_launches(torch, fused), (2 * 8 + 26) * S, S)
+    # flatten of one rank's 193 ragged bf16 tensors into the padded buckets
+    sizes = gpt2_small_sizes()
+    tens = [torch.empty(n, dtype=torch.int16, device="cuda") for n in sizes]
+    stream = torch.cuda.current_stream().cuda_stream
+    for i, x in enumerate(tens):
+        SG.fill(x.data_ptr(), synth.BF16, x.numel(), synth.key_of(2, 9, i, 0), 0, 1e-3, stream)
+    flat = torch.empty(run.P, dtype=torch.int16, device="cuda")
+    psi = sum(sizes)
+    out["flatten_gpt2_bf16"] = _entry(_time_launches(torch, lambda: Z.zero_flatten(run.plan, tens, Z.ZERO_BF16, flat)),
+                                      4 * psi + 2 * (run.P - psi), psi)
+    del run, tens, flat
+    free()
+    log("GPT-2 kernels done")
+
+    # Stage 3: one h = 8192 layer, N_d = 64 (gather_pack, then the fused step).
+    run = GpuRun(CONFIGS[5])
+    S, P = run.S, run.P
+    run.fill_grads(1, 0)
+    L = run.layers[0]
+    shards = list(L["shards"])
+    out["gather_pack_h8192_nd64"] = _entry(
+        _time_launches(torch, lambda: Z.zero_gather_pack(run.plan, shards, Z.ZERO_F16, run.full)), 4 * P, P)
+
+    def layer_step():
+        t[0] += 1
+        run.step(t[0], 0)          # gather_pack + fused step into the resident shard
+    out["stage3_layer_h8192_nd64"] = _entry(_time_launches(torch, layer_step), 4 * P + (2 * 64 + 26) * S, P)
+    del run, shards, L
+    free()
+    log("Stage-3 kernels done")
+    return out
+
+
+def _counter_means(path, kernel_substr, counter):
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {kernel_substr} in {path}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """Turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) of
+    the fused step and of the plain copy probe into HBM bytes per launch.  The
+    copy's known bytes give the scale of each counter."""
+    S = 117_187_520
+    copy_bytes = 4 << 30
+    cf, _ = _counter_means(copy_fetch_csv, "copyBuffer", "FETCH_SIZE")
+    cw, _ = _counter_means(copy_write_csv, "copyBuffer", "WRITE_SIZE")
+    kf = cf * 1024 / copy_bytes
+    kw = cw * 1024 / copy_bytes
+    ff, nf = _counter_means(fetch_csv, "step_vec_kernel", "FETCH_SIZE")
+    fw, nw = _counter_means(write_csv, "step_vec_kernel", "WRITE_SIZE")
+    reads, writes = ff * 1024 / kf, fw * 1024 / kw
+    rec = {"kernel_source_sha": kernel_source_sha(), "kernel": "step_vec_kernel<0, 2, 1, 64> (fused, bf16 grads, fp16 params)",
+           "workload": "7.5B-stage2, N_d=64, S=117187520", "fetch_kib_per_dispatch": ff, "write_kib_per_dispatch": fw,
+           "dispatches": [nf, nw], "copy_probe_fetch_kib": cf, "copy_probe_write_kib": cw,
+           "copy_probe_bytes_each_way": copy_bytes, "fetch_scale": kf, "write_scale": kw,
+           "hbm_read_bytes_per_launch": reads, "hbm_write_bytes_per_launch": writes,
+           "hbm_bytes_per_launch": reads + writes,
+           "algorithmic_bytes_per_launch": algorithmic_bytes_per_param(64) * S,
+           "read_bytes_per_element": reads / S, "write_bytes_per_element": writes / S}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 def copy_probe(torch):
     """A plain device copy of known size, for scaling rocprofv3's FETCH_SIZE and
     WRITE_SIZE counters to bytes: each dispatch reads and writes 4 GiB."""
@@ -100,7 +244,14 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="time a plain 4 GiB device copy (calibrates HBM byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernels", action="store_true",
+                    help="also time every entry point at its own workload (adds a 'kernels' object)")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="summarise rocprofv3 counter CSVs into the committed traffic record and exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the step is one rank's share, and its "
               "throughput at N GPUs is N times the one-GPU figure with no collective in the path; "
@@ -180,11 +331,14 @@ def main():
                      "algorithmic_bytes_per_launch": launch_bytes,
                      "avg_launch_ms": avg_launch_s * 1e3, "kernel": "step_vec_kernel (fused)"},
     }
+    del run
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if args.kernels:
+        out["kernels"] = measure_kernels(torch)
     if args.no_cpu_baseline:
         out["cpu_baseline"] = None
     else:
-        del run
-        torch.cuda.empty_cache()
         log("timing the CPU oracle on a sample ...")
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample)
     print(json.dumps(out), flush=True)
