@@ -109,6 +109,7 @@ def measure_kernels(torch):
     import zero_sharded_mixed_02_amd as Z
     import synth
     from synth import gpu as SG
+    from dataclasses import replace
     from synth.workloads import CONFIGS, GpuRun, gpt2_small_sizes
     out = {}
 
@@ -179,9 +180,41 @@ def measure_kernels(torch):
         t[0] += 1
         run.step(t[0], 0)          # gather_pack + fused step into the resident shard
     out["stage3_layer_h8192_nd64"] = _entry(_time_launches(torch, layer_step), 4 * P + (2 * 64 + 26) * S, P)
+
+    # All 8 layers: serial loop (one buffer) vs gathers on a side stream into
+    # two alternating buffers, overlapping step(l) with gather(l+1).
+    for layer in range(1, run.cfg.layers):
+        run.fill_grads(1, layer)
+    nl = run.cfg.layers
+    pass_bytes = nl * (4 * P + (2 * 64 + 26) * S)
+    res = {}
+    for name, pipelined in (("serial", False), ("pipelined", True)):
+        def loop(pipelined=pipelined):
+            t[0] += 1
+            run.layer_loop(t[0], pipelined)
+        res[name] = _entry(_time_launches(torch, loop, reps=10, warmup=2), pass_bytes, nl * P)
+    res["speedup"] = res["serial"]["ms"] / res["pipelined"]["ms"]
+    res["temp_buffer_bytes"] = {"serial": 2 * P, "pipelined": 4 * P}
+    out["stage3_8_layers_h8192_nd64"] = res
     del run, shards, L
     free()
     log("Stage-3 kernels done")
+
+    # Bucket size: the GPT-2 list under different caps (one launch holds up to
+    # 64 shard pieces; more buckets mean more launches).
+    sweep = {}
+    for cap in (1 << 18, 1 << 20, 1 << 22, 1 << 24, 1 << 26, 0):
+        run = GpuRun(replace(CONFIGS[2], bucket_cap=cap))
+        S = run.S
+        run.fill_grads(1)
+        e = _entry(_time_launches(torch, fused), (2 * 8 + 26) * S, S)
+        e["buckets"] = run.plan.n_buckets
+        e["launches"] = -(-run.plan.n_buckets // 64)
+        sweep[str(cap)] = e
+        del run
+        free()
+    out["bucket_cap_sweep_gpt2_nd8"] = sweep
+    log("bucket sweep done")
     return out
 
 

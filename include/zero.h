@@ -223,6 +223,29 @@ ZERO_API zero_status zero_adam_step(zero_plan_t plan, int32_t rank, const zero_a
 ZERO_API zero_status zero_gather_pack(zero_plan_t plan, const void* const* shards, zero_dtype dt, void* full,
                              void* stream);
 
+/*
+ * zero_reshard -- re-lay out a sharded per-element state for a different
+ * data-parallel degree or bucketing: the shard of rank dst_rank under dst_plan,
+ * assembled from all shards under src_plan.  The sharded optimizer state must
+ * survive a change of parallel degree -- a rank-local checkpoint restored at
+ * another N_d (concept page, design trade-off 4 and the checklist item on
+ * restoring rank-local shards after the parallel degree changes).
+ *   src_plan, dst_plan  plans over the SAME tensor list (sizes, order); n_d,
+ *               bucket_cap and shard_align may differ.
+ *   dst_rank    0 <= dst_rank < dst n_d.
+ *   src_shards  host array of src n_d device pointers, each src shard_total
+ *               elements (shard-local layout).
+ *   dt          element type (ZERO_F32 for master/m/v, 16-bit for params).
+ *   dst_shard   device buffer of dst shard_total elements: every real element
+ *               is copied from the source rank that owns the same tensor
+ *               element; padding is written as zero.
+ * A bit copy.  Errors: EINVAL for nulls, different tensor lists, a bad rank,
+ * misalignment, or dst_shard overlapping a source shard.
+ */
+ZERO_API zero_status zero_reshard(zero_plan_t src_plan, zero_plan_t dst_plan, int32_t dst_rank,
+                                  const void* const* src_shards, zero_dtype dt, void* dst_shard,
+                                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -224,6 +224,20 @@ def gather_pack(p: Plan, shards: Sequence[np.ndarray]) -> np.ndarray:
     return full
 
 
+def reshard(src: Plan, dst: Plan, dst_rank: int, src_shards: Sequence[np.ndarray]) -> np.ndarray:
+    """The shard of dst_rank under plan dst, from all shards under plan src
+    (same tensor list): materialise the flat buffer, split it back into the
+    tensors, flatten them with the new plan and take the rank's slices."""
+    assert src.tensor_numel == dst.tensor_numel
+    full = gather_pack(src, src_shards)
+    tensors = unflatten(src, full)
+    if tensors:
+        flat = flatten(dst, tensors)
+    else:
+        flat = np.zeros(dst.psi_pad, dtype=full.dtype)
+    return shard_of(dst, dst_rank, flat)
+
+
 # --------------------------------------------------------------------------
 # Arithmetic (through the C oracle)
 # --------------------------------------------------------------------------

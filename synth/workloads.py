@@ -207,6 +207,51 @@ class GpuRun:
         Z.zero_adam_step(self.plan, cfg.owner, cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.grad_scale, t,
                          self.src[layer], None, L["master"], L["m"], L["v"], dst, cfg.pdt, dst_full, stream)
 
+    def layer_loop(self, t: int, pipelined: bool = False):
+        """One Stage-3 pass over all layers: for each layer, gather_pack of
+        the layer's shards into a full-layer buffer, then the fused step into
+        the owner's resident shard.
+
+        pipelined=False: both on the current stream, one reused buffer.
+        pipelined=True: gathers run on a side stream into two alternating
+        buffers, so gather(l+1) overlaps step(l).  Events keep the order the
+        serial loop has: step(l) starts after gather(l) has read the owner's
+        pre-step shard, and gather(l+2) reuses a buffer only after step(l)
+        (standing in for the layer's compute that reads it) has finished."""
+        torch, Z, cfg = self.torch, self.Z, self.cfg
+        if not pipelined:
+            for layer in range(cfg.layers):
+                self.step(t, layer)
+            return
+        if getattr(self, "full2", None) is None:
+            self.full2 = torch.zeros_like(self.full)
+            self.side = torch.cuda.Stream(device=self.device)
+        bufs = [self.full, self.full2]
+        main = torch.cuda.current_stream(self.device)
+        side = self.side
+        side.wait_stream(main)
+        gathered = [torch.cuda.Event() for _ in range(cfg.layers)]
+        stepped = [torch.cuda.Event() for _ in range(cfg.layers)]
+
+        def gather(layer):
+            if layer >= 2:
+                side.wait_event(stepped[layer - 2])
+            Z.zero_gather_pack(self.plan, list(self.layers[layer]["shards"]), cfg.pdt, bufs[layer % 2],
+                               side.cuda_stream)
+            gathered[layer].record(side)
+
+        gather(0)
+        for layer in range(cfg.layers):
+            if layer + 1 < cfg.layers:
+                gather(layer + 1)
+            main.wait_event(gathered[layer])
+            L = self.layers[layer]
+            Z.zero_adam_step(self.plan, cfg.owner, cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.grad_scale, t,
+                             self.src[layer], None, L["master"], L["m"], L["v"], L["shards"][cfg.owner],
+                             cfg.pdt, False, main.cuda_stream)
+            stepped[layer].record(main)
+        main.wait_stream(side)
+
     def reduce(self, out, layer: int = 0, stream=None):
         self.Z.zero_shard_reduce(self.plan, self.cfg.owner, self.src[layer], self.cfg.grad_scale, out, stream)
 

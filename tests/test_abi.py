@@ -217,3 +217,21 @@ def test_single_hip_runtime_in_process():
             "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n") % ROOT
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True)
     assert out.stdout.strip() == "1"
+
+
+def test_reshard_rejects_bad_arguments(zero_lib):
+    Z = zero_lib
+    L = Z.load()
+    a = Z.zero_plan(1000, 4, [600, 400], 512, 8)
+    b = Z.zero_plan(1000, 3, [600, 400], 0, 1)
+    c = Z.zero_plan(1000, 3, [500, 500], 0, 1)
+    shards = (ctypes.c_void_p * 4)(*[BASE + q * (1 << 20) for q in range(4)])
+    out = BASE + (1 << 30)
+    assert L.zero_reshard(a.handle, c.handle, 0, shards, Z.ZERO_F32, out, None) == Z.ZERO_EINVAL
+    assert "tensor lists" in Z.zero_last_error()
+    assert L.zero_reshard(a.handle, b.handle, 3, shards, Z.ZERO_F32, out, None) == Z.ZERO_EINVAL
+    assert L.zero_reshard(None, b.handle, 0, shards, Z.ZERO_F32, out, None) == Z.ZERO_EINVAL
+    assert L.zero_reshard(a.handle, b.handle, 0, None, Z.ZERO_F32, out, None) == Z.ZERO_EINVAL
+    assert L.zero_reshard(a.handle, b.handle, 0, shards, 9, out, None) == Z.ZERO_EINVAL
+    assert L.zero_reshard(a.handle, b.handle, 0, shards, Z.ZERO_F32, BASE + 8, None) == Z.ZERO_EINVAL
+    assert L.zero_reshard(a.handle, b.handle, 0, shards, Z.ZERO_F32, out + 2, None) == Z.ZERO_EINVAL

@@ -104,3 +104,43 @@ def test_gather_pack(gpu, oracle_lib, zero_lib, es, align, n_d):
     torch.cuda.synchronize()
     got = full.cpu().numpy().view(np.uint16 if es == 2 else np.uint32)
     assert np.array_equal(got, O.gather_pack(op, shards))
+
+
+def _reshard_case(torch, gpu, O, Z, sizes, src_cfg, dst_cfg, es, seed):
+    psi = sum(sizes)
+    (n_d, cap, align), (n_d2, cap2, align2) = src_cfg, dst_cfg
+    zs, zd = Z.zero_plan(psi, n_d, sizes, cap, align), Z.zero_plan(psi, n_d2, sizes, cap2, align2)
+    os_, od = O.plan(psi, n_d, sizes, cap, align), O.plan(psi, n_d2, sizes, cap2, align2)
+    # source shards: bits at real elements, zero padding (what a sharded state holds)
+    tensors = [rand_bits(seed + t, n, es) for t, n in enumerate(sizes)]
+    flat = O.flatten(os_, tensors)
+    shards = [O.shard_of(os_, r, flat) for r in range(n_d)]
+    npdt, tdt = (np.int16, torch.int16) if es == 2 else (np.int32, torch.int32)
+    dev = [torch.from_numpy(s.view(npdt)).to(gpu) for s in shards]
+    dt = Z.ZERO_BF16 if es == 2 else Z.ZERO_F32
+    for r in range(n_d2):
+        out = torch.full((zd.shard_total,), -1, dtype=tdt, device=gpu)
+        Z.zero_reshard(zs, zd, r, dev, dt, out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().view(np.uint16 if es == 2 else np.uint32)
+        assert np.array_equal(got, O.reshard(os_, od, r, shards)), (src_cfg, dst_cfg, r)
+
+
+@pytest.mark.parametrize("es", [2, 4])
+def test_reshard_random_plans(gpu, oracle_lib, zero_lib, es):
+    import torch
+    rng = np.random.default_rng(90 + es)
+    for trial in range(8):
+        nt = int(rng.integers(1, 25))
+        sizes = [int(x) for x in rng.choice([0, 1, 5, 8, 63, 64, 100, 1000, 4097, 20000], size=nt)]
+        src = (int(rng.choice([1, 2, 3, 4, 8])), int(rng.choice([0, 500, 5000])), int(rng.choice([1, 8, 64])))
+        dst = (int(rng.choice([1, 2, 3, 5, 16])), int(rng.choice([0, 700, 9000])), int(rng.choice([1, 4, 64])))
+        say(f"[reshard] trial {trial}: {nt} tensors {src} -> {dst} es={es}")
+        _reshard_case(torch, gpu, oracle_lib, zero_lib, sizes, src, dst, es, 300 + trial)
+
+
+@pytest.mark.parametrize("src,dst", [((8, 1 << 24, 64), (16, 1 << 24, 64)), ((8, 1 << 24, 64), (3, 1 << 22, 1))])
+def test_reshard_gpt2_state(gpu, oracle_lib, zero_lib, src, dst):
+    import torch
+    say(f"[reshard] gpt2 fp32 state {src} -> {dst}")
+    _reshard_case(torch, gpu, oracle_lib, zero_lib, gpt2_small_sizes(), src, dst, 4, 700)

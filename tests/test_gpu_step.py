@@ -198,6 +198,38 @@ def test_stage3_layer_loop(gpu, oracle_lib, h, n_d, owner):
                 assert np.array_equal(got["shards"][q], want["shards"][q]), ("shard", q)
 
 
+def test_stage3_pipelined_loop_matches_serial(gpu, oracle_lib):
+    """The two-stream Stage-3 loop (gather of layer l+1 overlapping the step
+    of layer l, double-buffered) leaves exactly the state of the serial loop,
+    and its last two gathered buffers hold the oracle's materialised layers."""
+    from oracle.runner import OracleRun
+    from synth.workloads import layer_sizes
+    cfg = Config("stage3-pipe", tuple(layer_sizes(128)), n_d=16, gdt=BF16, pdt=F16, stage=3,
+                 owner=5, steps=2, layers=5, seed=23)
+    say("[stage3] pipelined vs serial, h=128 n_d=16 layers=5 steps=2")
+    serial, pipe, ref = GpuRun(cfg), GpuRun(cfg), OracleRun(cfg)
+    for t in range(1, cfg.steps + 1):
+        for layer in range(cfg.layers):
+            serial.fill_grads(t, layer)
+            pipe.fill_grads(t, layer)
+            ref.fill_grads(t, layer)
+        serial.layer_loop(t, pipelined=False)
+        pipe.layer_loop(t, pipelined=True)
+        for layer in range(cfg.layers):
+            ref.step(t, layer)
+        _sync()
+        for layer in range(cfg.layers):
+            a, b = serial.fetch(layer), pipe.fetch(layer)
+            for k in ("master", "m", "v"):
+                assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), (t, layer, k)
+            assert np.array_equal(a["shards"], b["shards"]), (t, layer)
+            assert_state({k: b[k] for k in ("master", "m", "v")}, ref.state(layer), cfg.pdt, f"L{layer}")
+        last, prev = cfg.layers - 1, cfg.layers - 2
+        bufs = [pipe.full.cpu().numpy().view(np.uint16), pipe.full2.cpu().numpy().view(np.uint16)]
+        assert np.array_equal(bufs[last % 2], ref.state(last)["gathered"])
+        assert np.array_equal(bufs[prev % 2], ref.state(prev)["gathered"])
+
+
 # ---------------------------------------------------------------------------
 # Special values and the output conversion
 # ---------------------------------------------------------------------------

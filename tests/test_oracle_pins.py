@@ -468,3 +468,34 @@ def test_single_rank_is_plain_mixed_precision_adam(oracle_lib):
     p2 = O.adam(O.value16(g, O.F16).astype(np.float32), w2, m2, v2,
                 O.adam_consts(LR, B1, B2, EPS, 1.0, 1), O.F16)
     assert np.array_equal(p1, p2) and np.array_equal(w1, w2)
+
+
+# ---------------------------------------------------------------------------
+# Reshard (a sharded state laid out for another N_d / bucketing)
+# ---------------------------------------------------------------------------
+
+def test_reshard_invariants(oracle_lib):
+    """Every tensor element keeps its value across a reshard, padding is
+    zero, resharding back gives the original shards, and resharding onto the
+    same plan is the identity."""
+    O = oracle_lib
+    rng = np.random.default_rng(41)
+    for (n_d, align, sizes, cap), (n_d2, align2, _, cap2) in zip(_random_plans(43, 80), _random_plans(47, 80)):
+        psi = sum(sizes)
+        src = O.plan(psi, n_d, sizes, cap, align)
+        dst = O.plan(psi, n_d2, sizes, cap2, align2)
+        tensors = [rng.standard_normal(n).astype(np.float32) for n in sizes]
+        flat = O.flatten(src, tensors) if sizes else np.zeros(src.psi_pad, np.float32)
+        shards = [O.shard_of(src, r, flat) for r in range(n_d)]
+        new = [O.reshard(src, dst, r, shards) for r in range(n_d2)]
+        new_flat = O.gather_pack(dst, new)
+        for t, x in enumerate(O.unflatten(dst, new_flat)):
+            assert np.array_equal(x, tensors[t])
+        for bk in dst.buckets:
+            assert not np.any(new_flat[bk.flat_off + bk.numel: bk.flat_off + bk.padded])
+        back = [O.reshard(dst, src, r, new) for r in range(n_d)]
+        for a, b in zip(back, shards):
+            assert np.array_equal(a, b)
+        same = [O.reshard(src, src, r, shards) for r in range(n_d)]
+        for a, b in zip(same, shards):
+            assert np.array_equal(a, b)

@@ -30,7 +30,7 @@ STATUS_NAMES = {0: "ZERO_OK", -1: "ZERO_EINVAL", -2: "ZERO_EUNSUPPORTED", -3: "Z
 # Names of every entry point include/zero.h declares.
 ENTRY_POINTS = ("zero_version", "zero_last_error", "zero_plan", "zero_plan_destroy",
                 "zero_plan_info", "zero_plan_bucket", "zero_plan_tensor", "zero_flatten",
-                "zero_shard_reduce", "zero_adam_step", "zero_gather_pack")
+                "zero_shard_reduce", "zero_adam_step", "zero_gather_pack", "zero_reshard")
 
 
 class ZeroError(RuntimeError):
@@ -98,6 +98,8 @@ def load():
                                  vp, vp, vp, vp, vp, i32, i32, vp]
     L.zero_gather_pack.restype = i32
     L.zero_gather_pack.argtypes = [vp, ctypes.POINTER(vp), i32, vp, vp]
+    L.zero_reshard.restype = i32
+    L.zero_reshard.argtypes = [vp, vp, i32, ctypes.POINTER(vp), i32, vp, vp]
     _lib = L
     return L
 
@@ -223,3 +225,9 @@ def zero_adam_step(plan: Plan, rank: int, lr: float, beta1: float, beta2: float,
 
 def zero_gather_pack(plan: Plan, shards: Sequence, dt: int, full, stream=None) -> None:
     _check(load().zero_gather_pack(plan.handle, _ptr_array(shards), dt, _addr(full), _stream(stream)))
+
+
+def zero_reshard(src_plan: Plan, dst_plan: Plan, dst_rank: int, src_shards: Sequence, dt: int, dst_shard,
+                 stream=None) -> None:
+    _check(load().zero_reshard(src_plan.handle, dst_plan.handle, dst_rank, _ptr_array(src_shards), dt,
+                               _addr(dst_shard), _stream(stream)))

@@ -379,6 +379,63 @@ zero_status zero_gather_pack(zero_plan_t p, const void* const* shards, zero_dtyp
   }
 }
 
+zero_status zero_reshard(zero_plan_t sp, zero_plan_t dp, int32_t dst_rank, const void* const* src_shards,
+                         zero_dtype dt, void* dst_shard, void* stream) {
+  try {
+    if (!sp || !dp) return fail(ZERO_EINVAL, "plan is NULL");
+    if (!valid_dt(dt)) return fail(ZERO_EINVAL, "unknown dtype %d", (int)dt);
+    if (sp->t_numel != dp->t_numel)
+      return fail(ZERO_EINVAL, "plans describe different tensor lists");
+    if (dst_rank < 0 || dst_rank >= dp->n_d)
+      return fail(ZERO_EINVAL, "dst_rank %d outside [0, %d)", dst_rank, dp->n_d);
+    const int es = esize(dt);
+    if (!src_shards) return fail(ZERO_EINVAL, "source shard pointer array is NULL");
+    if (!dst_shard && dp->shard_total > 0) return fail(ZERO_EINVAL, "dst_shard is NULL");
+    if (!aligned(dst_shard, es)) return fail(ZERO_EINVAL, "dst_shard is not element aligned");
+    const Range out = range_of(dst_shard, dp->shard_total, es, "dst_shard");
+    for (int32_t q = 0; q < sp->n_d; ++q) {
+      if (!src_shards[q] && sp->shard_total > 0) return fail(ZERO_EINVAL, "source shard %d is NULL", q);
+      if (!aligned(src_shards[q], es)) return fail(ZERO_EINVAL, "source shard %d is not element aligned", q);
+      if (overlap(out, range_of(src_shards[q], sp->shard_total, es, "source shard")))
+        return fail(ZERO_EINVAL, "dst_shard overlaps source shard %d", q);
+    }
+    // Walk the destination rank's owned ranges bucket by bucket: real
+    // elements come from whichever source rank owns the same tensor element,
+    // padding is written as zero.
+    std::vector<zk::CopyEnt> ents;
+    const int32_t nt = (int32_t)dp->t_numel.size();
+    int32_t t = 0;
+    for (size_t b = 0; b < dp->buckets.size(); ++b) {
+      const auto& B = dp->buckets[b];
+      const int64_t lo = B.flat_off + (int64_t)dst_rank * B.shard_numel;
+      const int64_t hi = lo + B.shard_numel;
+      while (t < nt && dp->t_bucket[t] < (int32_t)b) ++t;
+      for (int32_t u = t; u < nt && dp->t_bucket[u] == (int32_t)b; ++u) {
+        const int64_t x0 = std::max(lo, dp->t_off[u]);
+        const int64_t x1 = std::min(hi, dp->t_off[u] + dp->t_numel[u]);
+        if (x0 >= x1) continue;
+        const auto& SB = sp->buckets[sp->t_bucket[u]];
+        for (int64_t i = x0 - dp->t_off[u]; i < x1 - dp->t_off[u];) {
+          const int64_t rel = sp->t_off[u] + i - SB.flat_off;   // position inside the source bucket
+          const int64_t q = rel / SB.shard_numel;
+          const int64_t within = rel - q * SB.shard_numel;
+          const int64_t n = std::min(x1 - dp->t_off[u] - i, SB.shard_numel - within);
+          ents.push_back(zk::CopyEnt{(const char*)src_shards[q] + (SB.shard_off + within) * es,
+                                     B.shard_off + (dp->t_off[u] + i - lo), n, 0, 0});
+          i += n;
+        }
+      }
+      const int64_t pad_lo = std::max(lo, B.flat_off + B.numel);
+      if (pad_lo < hi) ents.push_back(zk::CopyEnt{nullptr, B.shard_off + (pad_lo - lo), hi - pad_lo, 0, 0});
+    }
+    return run_copies(ents, dst_shard, es, stream);
+  } catch (const std::bad_alloc&) {
+    return fail(ZERO_ENOMEM, "host allocation failed");
+  } catch (...) {
+    return fail(ZERO_EINVAL, "unexpected failure in zero_reshard");
+  }
+}
+
 zero_status zero_shard_reduce(zero_plan_t p, int32_t rank, const zero_grad_src* src,
                               double grad_scale, float* out, void* stream) {
   try {
