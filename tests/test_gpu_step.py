@@ -146,6 +146,39 @@ def test_reduce_more_ranks_than_one_launch(gpu, oracle_lib):
     assert ei.value.status == Z.ZERO_EUNSUPPORTED
 
 
+def test_misaligned_buffers_take_element_path(gpu, oracle_lib, zero_lib):
+    """Every buffer one element past a 16-byte boundary: the library must fall
+    back to the element kernel and still match the oracle bit for bit."""
+    import torch
+    from oracle.runner import OracleRun
+    Z = zero_lib
+    cfg = small_config(40_003, 5, F16, BF16, owner=4, steps=3, seed=29)
+    ref = OracleRun(cfg)
+    plan = Z.zero_plan(cfg.psi, cfg.n_d, list(cfg.sizes), cfg.bucket_cap, cfg.align)
+    S, P = plan.shard_total, plan.psi_pad
+
+    def view(n, dtype):
+        return torch.zeros(n + 8, dtype=dtype, device=gpu)[1:n + 1]
+
+    g = [view(S, torch.int16) for _ in range(cfg.n_d)]
+    w, m, v = view(S, torch.float32), view(S, torch.float32), view(S, torch.float32)
+    full = view(P, torch.int16)
+    w.copy_(torch.from_numpy(ref.layers[0]["master"]).to(gpu))
+    src = Z.GradSrc(cfg.gdt, g)
+    say("[misaligned] psi=40003 n_d=5 owner=4, all bases at +1 element")
+    for t in range(1, cfg.steps + 1):
+        ref.fill_grads(t)
+        for q in range(cfg.n_d):
+            g[q].copy_(torch.from_numpy(ref.layers[0]["slices"][q].view(np.int16)).to(gpu))
+        Z.zero_adam_step(plan, cfg.owner, cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.grad_scale, t, src, None,
+                         w, m, v, full, cfg.pdt, True)
+        ref.step(t)
+    _sync()
+    got = {"master": w.cpu().numpy(), "m": m.cpu().numpy(), "v": v.cpu().numpy(),
+           "full": full.cpu().numpy().view(np.uint16)}
+    assert_state(got, ref.state(), cfg.pdt, "misaligned")
+
+
 def test_empty_plan_is_a_no_op(gpu, zero_lib):
     import torch
     Z = zero_lib
