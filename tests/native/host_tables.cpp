@@ -1,0 +1,386 @@
+// Host-side launch tables of libzero, checked on the CPU.
+//
+// zero_api.cpp is compiled together with this file, which stands in for the
+// two kernel launchers: instead of launching, they replay the kernels' own
+// workgroup -> entry/segment indexing over the recorded argument blocks and
+// mark every element each launch would touch.  For random plans the test
+// checks that every destination element is written exactly once, that every
+// source element read lies inside its buffer, and that the step's segments
+// tile the owner's shard at the plan's offsets.  Built with g++ under
+// AddressSanitizer and UndefinedBehaviorSanitizer; no GPU is involved.
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <map>
+#include <random>
+#include <vector>
+
+#include "zero.h"
+#include "zero_internal.h"
+
+namespace {
+
+// Fake device address spaces: each buffer gets its own 1 TiB-aligned base so
+// an address identifies (buffer, byte offset).
+constexpr uint64_t kSpan = 1ull << 40;
+uint64_t fake_base(int id) { return (uint64_t)(id + 1) * kSpan; }
+
+struct Buffer {
+  int64_t bytes = 0;         // shift + elements * es
+  int64_t shift = 0;         // bytes before element 0
+  std::vector<uint8_t> writes;   // per element, saturating at 255
+  int es = 2;
+};
+std::map<int, Buffer> g_buf;   // id -> buffer
+int g_fail = 0;
+
+#define EXPECT(c, ...)                     \
+  do {                                     \
+    if (!(c)) {                            \
+      if (g_fail < 20) {                   \
+        fprintf(stderr, "FAIL: " __VA_ARGS__); \
+        fprintf(stderr, "\n");             \
+      }                                    \
+      ++g_fail;                            \
+    }                                      \
+  } while (0)
+
+// A buffer of elems elements of es bytes whose element 0 sits shift bytes
+// past a 1 TiB boundary (shift breaks 16-byte alignment on purpose).
+void* make(int id, int64_t elems, int es, int64_t shift = 0) {
+  Buffer& b = g_buf[id];
+  b.shift = shift;
+  b.bytes = shift + elems * es;
+  b.es = es;
+  b.writes.assign(elems, 0);
+  return (void*)(uintptr_t)(fake_base(id) + shift);
+}
+
+int buf_of(uint64_t addr) { return (int)(addr / kSpan) - 1; }
+
+void touch_read(uint64_t addr, int64_t bytes) {
+  const int id = buf_of(addr);
+  auto it = g_buf.find(id);
+  EXPECT(it != g_buf.end(), "read from unknown buffer %d", id);
+  if (it == g_buf.end()) return;
+  const int64_t off = (int64_t)(addr - fake_base(id));
+  EXPECT(off >= it->second.shift && off + bytes <= it->second.bytes, "read out of bounds: buffer %d off %lld len %lld size %lld",
+         id, (long long)off, (long long)bytes, (long long)it->second.bytes);
+}
+
+void touch_write(uint64_t addr, int64_t elems, int es) {
+  const int id = buf_of(addr);
+  auto it = g_buf.find(id);
+  EXPECT(it != g_buf.end(), "write to unknown buffer %d", id);
+  if (it == g_buf.end()) return;
+  const int64_t off = (int64_t)(addr - fake_base(id)) - it->second.shift;
+  EXPECT(off % es == 0, "misaligned write");
+  const int64_t e0 = off / es;
+  EXPECT(e0 >= 0 && e0 + elems <= (int64_t)it->second.writes.size(), "write out of bounds: buffer %d", id);
+  if (e0 < 0 || e0 + elems > (int64_t)it->second.writes.size()) return;
+  uint8_t* w = it->second.writes.data() + e0;
+  for (int64_t i = 0; i < elems; ++i) w[i] += w[i] != 255;
+}
+
+void expect_all_written_once(int id, const char* what) {
+  const auto& w = g_buf[id].writes;  // counts saturate at 255
+  for (size_t i = 0; i < w.size(); ++i)
+    if (w[i] != 1) {
+      EXPECT(false, "%s element %zu written %d times", what, i, (int)w[i]);
+      return;
+    }
+}
+
+struct StepRec {
+  zk::StepArgs a;
+  int mode, gdt, pdt, ndc, blocks;
+  bool vec;
+};
+std::vector<StepRec> g_steps;
+
+}  // namespace
+
+// ---- stand-ins for the launchers: replay the kernels' indexing ----------
+namespace zk {
+
+int launch_copy(const CopyArgs& a, int esz, int n_blocks, void*) {
+  // Entry of each block: last entry whose block_start <= block.
+  for (int e = 0; e < a.n_ent; ++e) {
+    const CopyEnt& en = a.ent[e];
+    const int b_end = e + 1 < a.n_ent ? a.ent[e + 1].block_start : n_blocks;
+    EXPECT(b_end > en.block_start, "entry with no blocks");
+    const uint64_t d0 = (uint64_t)(uintptr_t)a.dst + (uint64_t)en.dst_off * esz;
+    const uint64_t d1 = d0 + (uint64_t)en.n * esz;
+    const uint64_t u_first = d0 >> 4, u_end = (d1 + 15) >> 4;
+    const uint64_t covered = (uint64_t)(b_end - en.block_start) * kThreads * kCopyUnits;
+    EXPECT(u_first + covered >= u_end, "copy entry units not covered by its blocks");
+    EXPECT(covered < (u_end - u_first) + (uint64_t)kThreads * kCopyUnits, "copy entry has a block too many");
+    touch_write(d0, en.n, esz);
+    if (en.src) touch_read((uint64_t)(uintptr_t)en.src, en.n * esz);
+  }
+  EXPECT(a.n_ent <= kMaxCopy, "too many copy entries");
+  return 0;
+}
+
+int launch_step(const StepArgs& a, int mode, int gdt, int pdt, int ndc, bool vec, int n_blocks, void*) {
+  g_steps.push_back(StepRec{a, mode, gdt, pdt, ndc, n_blocks, vec});
+  return 0;
+}
+
+const char* hip_error_string(int) { return "stand-in"; }
+
+}  // namespace zk
+
+namespace {
+
+struct Rnd {
+  std::mt19937_64 g;
+  explicit Rnd(uint64_t s) : g(s) {}
+  int64_t pick(std::initializer_list<int64_t> v) { return *(v.begin() + g() % v.size()); }
+  int64_t range(int64_t lo, int64_t hi) { return lo + (int64_t)(g() % (uint64_t)(hi - lo)); }
+};
+
+struct PlanQ {
+  int64_t psi_pad, S;
+  int32_t nb, n_d;
+  std::vector<int64_t> off, numel, padded, sn, soff;
+};
+
+PlanQ query(zero_plan_t p) {
+  PlanQ q;
+  zero_plan_info(p, &q.psi_pad, &q.S, &q.nb, &q.n_d);
+  for (int b = 0; b < q.nb; ++b) {
+    int64_t o, n, pd, s, so;
+    zero_plan_bucket(p, b, &o, &n, &pd, &s, &so);
+    q.off.push_back(o); q.numel.push_back(n); q.padded.push_back(pd); q.sn.push_back(s); q.soff.push_back(so);
+  }
+  return q;
+}
+
+// Replays recorded step launches; returns per-shard-element coverage counts
+// and checks every segment against the plan.
+std::vector<uint8_t> replay_steps(const PlanQ& q, int rank, bool dst_full, uint64_t dst, int dst_es) {
+  std::vector<uint8_t> hits(q.S, 0);
+  for (const StepRec& r : g_steps) {
+    const int per_block = r.vec ? zk::kStepThreads * zk::kStepVec : zk::kThreads;
+    EXPECT(r.a.n_seg >= 1 && r.a.n_seg <= zk::kMaxSeg, "segment count");
+    EXPECT(r.a.n_ranks >= 0 && r.a.n_ranks <= zk::kMaxRanks, "rank count");
+    for (int s = 0; s < r.a.n_seg; ++s) {
+      const zk::StepSeg& g = r.a.seg[s];
+      const int b_end = s + 1 < r.a.n_seg ? r.a.seg[s + 1].block_start : r.blocks;
+      EXPECT((int64_t)(b_end - g.block_start) * per_block >= g.len, "segment not covered by its blocks");
+      EXPECT((int64_t)(b_end - g.block_start - 1) * per_block < g.len, "segment has a block too many");
+      EXPECT(g.len >= 1 && g.len <= zk::kSegMaxElems, "segment length %d", g.len);
+      if (r.vec) EXPECT(((g.shard_off | g.full_off | g.dst_off | g.len) & 7) == 0, "vector segment not 8-aligned");
+      int b = -1;
+      for (int k = 0; k < q.nb; ++k)
+        if (g.shard_off >= q.soff[k] && g.shard_off + g.len <= q.soff[k] + q.sn[k]) b = k;
+      EXPECT(b >= 0, "segment not inside one bucket");
+      if (b < 0) continue;
+      const int64_t own = q.off[b] + (int64_t)rank * q.sn[b] + (g.shard_off - q.soff[b]);
+      EXPECT(g.full_off == own, "full_off %lld != owner range %lld", (long long)g.full_off, (long long)own);
+      EXPECT(g.dst_off == (dst_full ? own : g.shard_off), "dst_off wrong");
+      for (int64_t i = 0; i < g.len; ++i) hits[g.shard_off + i] += hits[g.shard_off + i] != 255;
+      touch_write(dst + (uint64_t)g.dst_off * dst_es, g.len, dst_es);
+      for (int k = 0; k < r.a.n_ranks; ++k) {
+        const bool full = (r.a.full_mask[k >> 5] >> (k & 31)) & 1u;
+        touch_read((uint64_t)(uintptr_t)r.a.grad[k] + (full ? g.full_off : g.shard_off) * 2, g.len * 2);
+      }
+      if (r.mode == zk::kFromReduced) touch_read((uint64_t)(uintptr_t)r.a.reduced + g.shard_off * 4, g.len * 4);
+      if (r.mode != zk::kReduceOnly)
+        for (const float* x : {r.a.master, r.a.m, r.a.v}) touch_read((uint64_t)(uintptr_t)x + g.shard_off * 4, g.len * 4);
+    }
+  }
+  return hits;
+}
+
+void expect_hits(const std::vector<uint8_t>& hits, int want, const char* what) {
+  for (size_t j = 0; j < hits.size(); ++j)
+    if (hits[j] != want) {
+      EXPECT(false, "%s: shard element %zu covered %d times, want %d", what, j, (int)hits[j], want);
+      return;
+    }
+}
+
+void check_step(zero_plan_t p, int rank, bool dst_full, bool use_full_grads, int64_t shift) {
+  const PlanQ q = query(p);
+  g_buf.clear();
+  g_steps.clear();
+  const bool fused = q.n_d <= ZERO_MAX_RANKS;
+  std::vector<const void*> ptrs(q.n_d);
+  std::vector<uint8_t> isf(q.n_d);
+  for (int r = 0; r < q.n_d; ++r) {
+    isf[r] = use_full_grads && (r % 2 == 0);
+    ptrs[r] = make(100 + r, isf[r] ? q.psi_pad : q.S, 2);
+  }
+  float* w = (float*)make(1, q.S, 4, shift);
+  float* m = (float*)make(2, q.S, 4);
+  float* v = (float*)make(3, q.S, 4);
+  void* dst = make(4, dst_full ? q.psi_pad : q.S, 2);
+  const float* red = fused ? nullptr : (const float*)make(5, q.S, 4);
+  zero_grad_src src = {ZERO_BF16, q.n_d, ptrs.data(), isf.data()};
+  zero_adam_hyper hp = {1e-4, 0.9, 0.999, 1e-8, 0.5};
+  const zero_status st = zero_adam_step(p, rank, &hp, 3, fused ? &src : nullptr, red, w, m, v, dst, ZERO_F16,
+                                        dst_full ? 1 : 0, nullptr);
+  EXPECT(st == ZERO_OK, "zero_adam_step failed: %s", zero_last_error());
+  for (const StepRec& r : g_steps) {
+    EXPECT(r.mode == (fused ? zk::kFused : zk::kFromReduced), "step mode");
+    if (shift) EXPECT(!r.vec, "vector kernel chosen for a misaligned buffer");
+    if (fused) {
+      EXPECT(r.a.n_ranks == q.n_d, "fused launch has %d ranks", r.a.n_ranks);
+      for (int k = 0; k < q.n_d; ++k) {
+        EXPECT(r.a.grad[k] == ptrs[k], "rank %d pointer", k);
+        EXPECT((bool)((r.a.full_mask[k >> 5] >> (k & 31)) & 1u) == (bool)isf[k], "rank %d full flag", k);
+      }
+    }
+  }
+  expect_hits(replay_steps(q, rank, dst_full, (uint64_t)(uintptr_t)dst, 2), 1, "adam step");
+  if (dst_full) {
+    // Only the owner's ranges of the full buffer are written, each once.
+    const auto& wr = g_buf[4].writes;
+    for (int k = 0; k < q.nb; ++k)
+      for (int64_t i = 0; i < q.padded[k]; ++i) {
+        const int64_t pos = q.off[k] + i;
+        const bool owned = i >= (int64_t)rank * q.sn[k] && i < (int64_t)(rank + 1) * q.sn[k];
+        if (wr[pos] != (owned ? 1 : 0)) {
+          EXPECT(false, "full buffer element %lld written %d times (owned %d)", (long long)pos, (int)wr[pos], owned);
+          k = q.nb;
+          break;
+        }
+      }
+  } else {
+    expect_all_written_once(4, "shard destination");
+  }
+}
+
+// zero_shard_reduce: one pass per group of up to 128 ranks, each covering the
+// shard once; the first pass starts the fold, later ones continue it from the
+// output, and only the last applies the scale.
+void check_reduce(zero_plan_t p, int rank, int64_t shift) {
+  const PlanQ q = query(p);
+  g_buf.clear();
+  g_steps.clear();
+  std::vector<const void*> ptrs(q.n_d);
+  for (int r = 0; r < q.n_d; ++r) ptrs[r] = make(100 + r, q.S, 2, r == 1 ? shift : 0);
+  float* out = (float*)make(1, q.S, 4);
+  zero_grad_src src = {ZERO_F16, q.n_d, ptrs.data(), nullptr};
+  EXPECT(zero_shard_reduce(p, rank, &src, 0.25, out, nullptr) == ZERO_OK, "reduce failed: %s", zero_last_error());
+  const int groups = (q.n_d + zk::kMaxRanks - 1) / zk::kMaxRanks;
+  int ranks_seen = 0, last_group = -1;
+  for (const StepRec& r : g_steps) {
+    EXPECT(r.mode == zk::kReduceOnly, "reduce mode");
+    if (shift && q.n_d > 1) EXPECT(!r.vec, "vector kernel chosen for a misaligned gradient");
+    const int g0 = (int)(std::find(ptrs.begin(), ptrs.end(), r.a.grad[0]) - ptrs.begin());
+    EXPECT(g0 % zk::kMaxRanks == 0, "group starts at rank %d", g0);
+    const int grp = g0 / zk::kMaxRanks;
+    if (grp != last_group) ranks_seen += r.a.n_ranks, last_group = grp;
+    EXPECT(r.a.n_ranks == std::min(zk::kMaxRanks, q.n_d - g0), "group size");
+    for (int k = 0; k < r.a.n_ranks; ++k) EXPECT(r.a.grad[k] == ptrs[g0 + k], "group rank pointer");
+    EXPECT(((r.a.flags & zk::kFlagInitFromOut) != 0) == (grp > 0), "init-from-out flag");
+    EXPECT(((r.a.flags & zk::kFlagApplyScale) != 0) == (grp == groups - 1), "scale flag");
+    EXPECT(r.a.c[8] == 0.25f, "scale constant");
+  }
+  EXPECT(q.S == 0 || ranks_seen == q.n_d, "ranks folded %d of %d", ranks_seen, q.n_d);
+  expect_hits(replay_steps(q, rank, false, (uint64_t)(uintptr_t)out, 4), groups, "reduce");
+}
+
+void check_copies(zero_plan_t p, const std::vector<int64_t>& sizes, Rnd& rnd) {
+  const PlanQ q = query(p);
+  const int es = rnd.pick({2, 4}) == 2 ? 2 : 4;
+  const zero_dtype dt = es == 2 ? ZERO_BF16 : ZERO_F32;
+  // flatten: tensors (possibly misaligned by whole elements) -> flat
+  g_buf.clear();
+  std::vector<const void*> tens(sizes.size());
+  for (size_t t = 0; t < sizes.size(); ++t) {
+    char* base = (char*)make(200 + (int)t, sizes[t] + 8, es);
+    tens[t] = sizes[t] ? base + es * rnd.range(0, 8) : nullptr;
+  }
+  void* flat = make(1, q.psi_pad, es);
+  EXPECT(zero_flatten(p, tens.data(), dt, flat, nullptr) == ZERO_OK, "flatten failed: %s", zero_last_error());
+  expect_all_written_once(1, "flat");
+  // gather_pack: shards -> full
+  g_buf.clear();
+  std::vector<const void*> sh(q.n_d);
+  for (int r = 0; r < q.n_d; ++r) sh[r] = make(300 + r, q.S, es);
+  void* full = make(2, q.psi_pad, es);
+  EXPECT(zero_gather_pack(p, sh.data(), dt, full, nullptr) == ZERO_OK, "gather failed: %s", zero_last_error());
+  expect_all_written_once(2, "full");
+}
+
+void check_reshard(const std::vector<int64_t>& sizes, int64_t psi, Rnd& rnd) {
+  zero_plan_t a, b;
+  const int na = (int)rnd.pick({1, 2, 3, 4, 8, 16, 64}), nb = (int)rnd.pick({1, 2, 3, 5, 16});
+  zero_plan(psi, na, sizes.data(), (int32_t)sizes.size(), rnd.pick({0, 7, 64, 1000}), (int32_t)rnd.pick({1, 8, 64}), &a);
+  zero_plan(psi, nb, sizes.data(), (int32_t)sizes.size(), rnd.pick({0, 9, 500}), (int32_t)rnd.pick({1, 4, 64}), &b);
+  const PlanQ qa = query(a), qb = query(b);
+  for (int r = 0; r < nb; ++r) {
+    g_buf.clear();
+    std::vector<const void*> sh(na);
+    for (int k = 0; k < na; ++k) sh[k] = make(400 + k, qa.S, 4);
+    void* out = make(1, qb.S, 4);
+    EXPECT(zero_reshard(a, b, r, sh.data(), ZERO_F32, out, nullptr) == ZERO_OK, "reshard failed: %s",
+           zero_last_error());
+    expect_all_written_once(1, "reshard destination");
+  }
+  zero_plan_destroy(a);
+  zero_plan_destroy(b);
+}
+
+}  // namespace
+
+int main() {
+  Rnd rnd(12345);
+  int cases = 0;
+  for (int it = 0; it < 300; ++it) {
+    const int nt = (int)rnd.range(0, 12);
+    std::vector<int64_t> sizes(nt);
+    int64_t psi = 0;
+    for (auto& s : sizes) {
+      s = rnd.pick({0, 1, 3, 8, 17, 64, 100, 1000, 4099});
+      psi += s;
+    }
+    const int n_d = (int)rnd.pick({1, 2, 3, 4, 5, 8, 16, 64, 130});
+    zero_plan_t p;
+    if (zero_plan(psi, n_d, sizes.data(), nt, rnd.pick({0, 1, 50, 1000, 100000}), (int32_t)rnd.pick({1, 8, 64}),
+                  &p) != ZERO_OK) {
+      EXPECT(false, "plan failed: %s", zero_last_error());
+      continue;
+    }
+    const PlanQ q = query(p);
+    const int rank = (int)rnd.range(0, n_d);
+    check_step(p, rank, rnd.g() & 1, rnd.g() & 1, (rnd.g() % 4 == 0) ? 4 : 0);
+    check_reduce(p, rank, (rnd.g() % 4 == 0) ? 2 : 0);
+    check_copies(p, sizes, rnd);
+    if (nt) check_reshard(sizes, psi, rnd);
+    zero_plan_destroy(p);
+    ++cases;
+    (void)q;
+  }
+  // More buckets than one launch's segment table.
+  {
+    std::vector<int64_t> sizes(300);
+    for (size_t i = 0; i < sizes.size(); ++i) sizes[i] = 8 + (int64_t)(i % 7) * 24;
+    int64_t psi = 0;
+    for (auto s : sizes) psi += s;
+    zero_plan_t p;
+    zero_plan(psi, 3, sizes.data(), (int32_t)sizes.size(), 1, 8, &p);
+    check_step(p, 2, true, true, 0);
+    check_reduce(p, 1, 0);
+    check_copies(p, sizes, rnd);
+    zero_plan_destroy(p);
+  }
+  // A bucket whose shard is longer than 2^28 elements: split into pieces.
+  {
+    std::vector<int64_t> sizes = {((int64_t)1 << 28) + 40, 5, 1000};
+    zero_plan_t p;
+    zero_plan(sizes[0] + sizes[1] + sizes[2], 1, sizes.data(), 3, 0, 64, &p);
+    check_step(p, 0, true, false, 0);
+    check_reduce(p, 0, 0);
+    zero_plan_destroy(p);
+  }
+  printf("%d random plans checked, %d failures\n", cases, g_fail);
+  return g_fail ? 1 : 0;
+}
