@@ -218,6 +218,72 @@ def measure_kernels(torch):
     return out
 
 
+# Write-window settings tried per workload: periods (ticks of the 100 MHz
+# real-time counter) x opening fractions, around the automatic choice.
+WINDOW_GRIDS = {
+    "fused_7.5B-stage2": ((3000, 4000, 5000, 6000), (1 / 16, 1 / 11, 1 / 8)),
+    "reduce_7.5B_nd64": ((1000, 1500, 2000, 2500, 3000), (1 / 32, 1 / 16, 1 / 8)),
+    "fused_13B-stage1": ((1000, 1400, 2000, 2500), (1 / 8, 1 / 4, 3 / 8)),
+    "stage3_layer_h8192_nd64": ((3000, 4000, 5000, 6000), (1 / 16, 1 / 8)),
+    "fused_gpt2-small": ((500, 1000), (1 / 4, 1 / 2)),
+}
+
+
+def measure_windows(torch):
+    """The step under different write windows (period, open ticks of the
+    100 MHz real-time counter; (0, 0) = stores at once; "auto" = the library's
+    choice) on the fused 7.5B, 13B, Stage-3-layer and GPT-2 workloads and the
+    7.5B reduce-only launch.  Results are bit-identical under every setting;
+    only the store timing changes."""
+    import zero_sharded_mixed_02_amd as Z
+    from synth.workloads import CONFIGS, GpuRun
+    t = [0]
+    out = {}
+
+    def sweep(name, fn, nbytes, elems, reps):
+        res = {}
+        periods, fracs = WINDOW_GRIDS[name]
+        grid = [(0, 0)] + [(p, max(1, int(p * f))) for p in periods for f in fracs] + [("auto", None)]
+        for per, opn in grid:
+            Z.zero_set_write_window(-1 if per == "auto" else per, opn or 0)
+            key = "auto" if per == "auto" else "off" if per == 0 else f"{per}/{opn}"
+            res[key] = _entry(_time_launches(torch, fn, reps=reps), nbytes, elems)
+        Z.zero_set_write_window(-1)
+        best = min((k for k in res if k != "auto"), key=lambda k: res[k]["ms"])
+        out[name] = {"ms": {k: round(v["ms"], 4) for k, v in res.items()},
+                     "frac_hbm_peak": {k: round(v["frac_hbm_peak"], 4) for k, v in res.items()},
+                     "best": best}
+        log(f"{name}: off {res['off']['ms']:.3f} ms, best {best} {res[best]['ms']:.3f} ms, "
+            f"auto {res['auto']['ms']:.3f} ms")
+
+    def fused_of(run, layer=None):
+        def f():
+            t[0] += 1
+            if layer is None:
+                run.step(t[0])
+            else:
+                run.step(t[0], layer)
+        return f
+
+    for num, reps in ((3, 10), (4, 4), (5, 10), (2, 20)):
+        run = GpuRun(CONFIGS[num])
+        n_d, S = run.cfg.n_d, run.S
+        if num == 5:
+            run.fill_grads(1, 0)
+            sweep("stage3_layer_h8192_nd64", fused_of(run, 0), 4 * run.P + (2 * n_d + 26) * S, run.P, reps)
+        else:
+            run.fill_grads(1)
+            sweep(f"fused_{run.cfg.name}", fused_of(run), (2 * n_d + 26) * S, S, reps)
+        if num == 3:
+            red = torch.empty(S, dtype=torch.float32, device="cuda")
+            sweep("reduce_7.5B_nd64", lambda: run.reduce(red), (2 * n_d + 4) * S, S, reps)
+            del red
+        del run
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
 def _counter_means(path, kernel_substr, counter):
     import csv
     vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
@@ -279,6 +345,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels", action="store_true",
                     help="also time every entry point at its own workload (adds a 'kernels' object)")
+    ap.add_argument("--window-sweep", action="store_true",
+                    help="also time the step under a grid of write windows (adds a 'write_windows' object)")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="summarise rocprofv3 counter CSVs into the committed traffic record and exit")
     args = ap.parse_args()
@@ -363,12 +431,15 @@ def main():
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": launch_bytes,
                      "avg_launch_ms": avg_launch_s * 1e3, "kernel": "step_vec_kernel (fused)"},
+        "write_window": "automatic (library default)",
     }
     del run
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     if args.kernels:
         out["kernels"] = measure_kernels(torch)
+    if args.window_sweep:
+        out["write_windows"] = measure_windows(torch)
     if args.no_cpu_baseline:
         out["cpu_baseline"] = None
     else:

@@ -246,6 +246,29 @@ ZERO_API zero_status zero_reshard(zero_plan_t src_plan, zero_plan_t dst_plan, in
                                   const void* const* src_shards, zero_dtype dt, void* dst_shard,
                                   void* stream);
 
+/*
+ * zero_set_write_window -- scheduling of the stores of zero_shard_reduce and
+ * of the fused zero_adam_step (not an operation of the pages: a tuning knob of
+ * this library; results are bit-identical whatever it is set to).
+ * The fused step reads about ten bytes of gradient for each byte it writes.
+ * With a write window, a wave whose results are ready holds its stores until
+ * the GPU's constant-rate real-time counter (100 MHz on MI355X: one tick is
+ * 10 ns) is within the first open_ticks of a period_ticks-long period, so the
+ * device's writes reach HBM in bursts rather than as a thin stream between
+ * the reads.
+ *   period_ticks  -1: automatic (the default): the library picks the window
+ *                 per launch from the rank count and the launch size, and
+ *                 uses none for small launches;
+ *                  0: no window, stores issue as soon as results are ready;
+ *                 1..100000: this period for every fused or reduce launch.
+ *   open_ticks    1..period_ticks when period_ticks > 0; ignored otherwise.
+ * The setting is process-wide, applies to launches issued after the call and
+ * is safe to change from any thread.  Adam from a `reduced` buffer, the
+ * element-wise (unaligned) kernels and the copy kernels never wait.
+ * Errors: EINVAL for values outside these ranges (the setting is unchanged).
+ */
+ZERO_API zero_status zero_set_write_window(int64_t period_ticks, int64_t open_ticks);
+
 #ifdef __cplusplus
 }
 #endif

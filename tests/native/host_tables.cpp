@@ -15,6 +15,7 @@
 
 #include <algorithm>
 #include <map>
+#include <utility>
 #include <random>
 #include <vector>
 
@@ -132,6 +133,10 @@ int launch_step(const StepArgs& a, int mode, int gdt, int pdt, int ndc, bool vec
 
 const char* hip_error_string(int) { return "stand-in"; }
 
+// Stand-in occupancy: 4 workgroups per CU for the fused kernel, 2 for the
+// reduce kernel (their register use on gfx950), 256 CUs.
+int resident_blocks(int mode, int, int, int, bool) { return mode == kFused ? 1024 : 512; }
+
 }  // namespace zk
 
 namespace {
@@ -162,9 +167,32 @@ PlanQ query(zero_plan_t p) {
 
 // Replays recorded step launches; returns per-shard-element coverage counts
 // and checks every segment against the plan.
+// The write window the launcher must have chosen: none for Adam from the
+// reduced gradient and for the element kernel; otherwise the forced setting,
+// or, automatically, none for launches under 2^23 elements (the large
+// automatic cases are checked by value in main).
+int64_t g_forced_period = -1, g_forced_open = 0;
+
+void check_window(const StepRec& r) {
+  int64_t elems = 0;
+  for (int s = 0; s < r.a.n_seg; ++s) elems += r.a.seg[s].len;
+  uint32_t p = 0, o = 0;
+  if (r.vec && r.mode != zk::kFromReduced) {
+    if (g_forced_period >= 0) {
+      p = (uint32_t)g_forced_period;
+      o = g_forced_period ? (uint32_t)g_forced_open : 0;
+    } else if (elems >= (int64_t(1) << 23)) {
+      return;
+    }
+  }
+  EXPECT(r.a.win_period == p && r.a.win_open == o, "write window (%u, %u), want (%u, %u)", r.a.win_period,
+         r.a.win_open, p, o);
+}
+
 std::vector<uint8_t> replay_steps(const PlanQ& q, int rank, bool dst_full, uint64_t dst, int dst_es) {
   std::vector<uint8_t> hits(q.S, 0);
   for (const StepRec& r : g_steps) {
+    check_window(r);
     const int per_block = r.vec ? zk::kStepThreads * zk::kStepVec : zk::kThreads;
     EXPECT(r.a.n_seg >= 1 && r.a.n_seg <= zk::kMaxSeg, "segment count");
     EXPECT(r.a.n_ranks >= 0 && r.a.n_ranks <= zk::kMaxRanks, "rank count");
@@ -358,6 +386,72 @@ int main() {
     zero_plan_destroy(p);
     ++cases;
     (void)q;
+  }
+  // Write-window setting: range checks, forced values reach every fused and
+  // reduce launch, and -1 restores the automatic choice.
+  EXPECT(zero_set_write_window(-2, 0) == ZERO_EINVAL, "period -2 accepted");
+  EXPECT(zero_set_write_window(100001, 1) == ZERO_EINVAL, "period above 1 ms accepted");
+  EXPECT(zero_set_write_window(100, 0) == ZERO_EINVAL, "open 0 accepted");
+  EXPECT(zero_set_write_window(100, 101) == ZERO_EINVAL, "open > period accepted");
+  for (const auto& pw : {std::pair<int64_t, int64_t>{400, 100}, {0, 0}, {100000, 100000}, {-1, 0}}) {
+    EXPECT(zero_set_write_window(pw.first, pw.second) == ZERO_OK, "window setting refused");
+    g_forced_period = pw.first;
+    g_forced_open = pw.second;
+    std::vector<int64_t> sizes = {4096, 800, 64 * 40};
+    zero_plan_t p;
+    zero_plan(sizes[0] + sizes[1] + sizes[2], 40, sizes.data(), 3, 0, 8, &p);
+    check_step(p, 5, true, false, 0);
+    check_step(p, 6, false, true, 4);
+    check_reduce(p, 7, 0);
+    zero_plan_destroy(p);
+  }
+  // The automatic window of a large launch: 64 ranks, 2^25 + 4096 elements
+  // per shard (only the tables are built; no memory behind the pointers).
+  {
+    std::vector<int64_t> sizes = {((int64_t)1 << 25) * 64 + 4096 * 64};
+    zero_plan_t p;
+    zero_plan(sizes[0], 64, sizes.data(), 1, 0, 64, &p);
+    g_steps.clear();
+    const PlanQ q = query(p);
+    std::vector<const void*> ptrs(64);
+    for (int r = 0; r < 64; ++r) ptrs[r] = (const void*)(uintptr_t)fake_base(100 + r);
+    zero_grad_src src = {ZERO_BF16, 64, ptrs.data(), nullptr};
+    zero_adam_hyper hp = {1e-4, 0.9, 0.999, 1e-8, 1.0 / 64};
+    EXPECT(zero_adam_step(p, 3, &hp, 1, &src, nullptr, (float*)(uintptr_t)fake_base(1),
+                          (float*)(uintptr_t)fake_base(2), (float*)(uintptr_t)fake_base(3),
+                          (void*)(uintptr_t)fake_base(4), ZERO_F16, 1, nullptr) == ZERO_OK,
+           "large step failed: %s", zero_last_error());
+    // 1024 resident workgroups x 4096 elements x 154 bytes at 6.5 TB/s, halved,
+    // in 10 ns ticks: 4968; open for the written 14/154 of it: 451.
+    EXPECT(g_steps.size() == 1 && g_steps[0].a.win_period == 4968 && g_steps[0].a.win_open == 451,
+           "automatic window of a large fused launch: (%u, %u)", g_steps.empty() ? 0u : g_steps[0].a.win_period,
+           g_steps.empty() ? 0u : g_steps[0].a.win_open);
+    EXPECT(zero_adam_step(p, 3, &hp, 1, nullptr, (const float*)(uintptr_t)fake_base(5),
+                          (float*)(uintptr_t)fake_base(1), (float*)(uintptr_t)fake_base(2),
+                          (float*)(uintptr_t)fake_base(3), (void*)(uintptr_t)fake_base(4), ZERO_F16, 1,
+                          nullptr) == ZERO_OK, "large from-reduced step failed: %s", zero_last_error());
+    EXPECT(g_steps.size() == 2 && g_steps[1].a.win_period == 0, "window on Adam from the reduced gradient");
+    // The reduction: 512 resident x 4096 x 132 bytes -> 2129 ticks, open 1/16.
+    zero_grad_src src16 = {ZERO_BF16, 64, ptrs.data(), nullptr};
+    EXPECT(zero_shard_reduce(p, 3, &src16, 1.0 / 64, (float*)(uintptr_t)fake_base(5), nullptr) == ZERO_OK,
+           "large reduce failed: %s", zero_last_error());
+    EXPECT(g_steps.size() == 3 && g_steps[2].a.win_period == 2129 && g_steps[2].a.win_open == 133,
+           "automatic window of a large reduce launch: (%u, %u)", g_steps.size() < 3 ? 0u : g_steps[2].a.win_period,
+           g_steps.size() < 3 ? 0u : g_steps[2].a.win_open);
+    // Few ranks: no automatic window.
+    std::vector<int64_t> s8 = {((int64_t)1 << 25) * 8};
+    zero_plan_t p8;
+    zero_plan(s8[0], 8, s8.data(), 1, 0, 64, &p8);
+    zero_grad_src src8 = {ZERO_BF16, 8, ptrs.data(), nullptr};
+    g_steps.clear();
+    EXPECT(zero_adam_step(p8, 0, &hp, 1, &src8, nullptr, (float*)(uintptr_t)fake_base(1),
+                          (float*)(uintptr_t)fake_base(2), (float*)(uintptr_t)fake_base(3),
+                          (void*)(uintptr_t)fake_base(4), ZERO_F16, 1, nullptr) == ZERO_OK,
+           "n_d=8 step failed: %s", zero_last_error());
+    EXPECT(g_steps.size() == 1 && g_steps[0].a.win_period == 0, "automatic window with 8 ranks");
+    zero_plan_destroy(p8);
+    (void)q;
+    zero_plan_destroy(p);
   }
   // More buckets than one launch's segment table.
   {

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol(zero_lib):
 
 
 def test_version(zero_lib):
-    assert zero_lib.zero_version() == 100
+    assert zero_lib.zero_version() == 101
 
 
 def _plan_tuple_lib(Z, p, n_tensors):
@@ -235,3 +235,14 @@ def test_reshard_rejects_bad_arguments(zero_lib):
     assert L.zero_reshard(a.handle, b.handle, 0, shards, 9, out, None) == Z.ZERO_EINVAL
     assert L.zero_reshard(a.handle, b.handle, 0, shards, Z.ZERO_F32, BASE + 8, None) == Z.ZERO_EINVAL
     assert L.zero_reshard(a.handle, b.handle, 0, shards, Z.ZERO_F32, out + 2, None) == Z.ZERO_EINVAL
+
+
+def test_write_window_setting(zero_lib):
+    """zero_set_write_window range checks (no launch involved)."""
+    Z = zero_lib
+    for bad in ((-2, 0), (100_001, 1), (100, 0), (100, 101)):
+        with pytest.raises(Z.ZeroError) as ei:
+            Z.zero_set_write_window(*bad)
+        assert ei.value.status == Z.ZERO_EINVAL
+    for good in ((6000, 750), (1, 1), (100_000, 100_000), (0, 0), (-1, 0)):
+        Z.zero_set_write_window(*good)

@@ -146,6 +146,39 @@ def test_reduce_more_ranks_than_one_launch(gpu, oracle_lib):
     assert ei.value.status == Z.ZERO_EUNSUPPORTED
 
 
+@pytest.mark.parametrize("window", [(0, 0), (50, 10), (300, 1), (-1, 0)])
+def test_write_windows_change_nothing(gpu, oracle_lib, zero_lib, window):
+    """The store timing of zero_set_write_window leaves every result bit
+    unchanged: the fused step at n_d = 64 and 16 (compiled rank counts) and 5
+    (runtime count), and the reduction at n_d = 200 (two launches), each equal
+    to the oracle with windows off, forced (including a 10 ns opening in a
+    3 us period) and automatic."""
+    import torch
+    import oracle as O
+    from oracle.runner import OracleRun
+    Z = zero_lib
+    say(f"[write window] period/open = {window}")
+    Z.zero_set_write_window(*window)
+    try:
+        for name in ("nd64-lastrank", "stage1-nd16-allfull-mix", "stage1-nd5-somefull"):
+            cfg = SMALL_CASES[name]
+            say(f"  fused {name}")
+            run, ref = run_pair(cfg)
+            assert_state(run.fetch(), ref.state(), cfg.pdt, f"{name} window {window}")
+        cfg = small_config(100_000, 200, BF16, F16, owner=7, steps=1, seed=17, align=8)
+        say("  reduce n_d=200")
+        run, ref = GpuRun(cfg), OracleRun(cfg)
+        red = torch.empty(run.S, dtype=torch.float32, device=gpu)
+        run.fill_grads(1)
+        ref.fill_grads(1)
+        run.reduce(red)
+        _sync()
+        want = O.reduce(ref.layers[0]["slices"], cfg.gdt, float(np.float32(cfg.grad_scale)))
+        assert_f32(red.cpu().numpy(), want, "reduced", bitwise=True)
+    finally:
+        Z.zero_set_write_window(-1)
+
+
 def test_misaligned_buffers_take_element_path(gpu, oracle_lib, zero_lib):
     """Every buffer one element past a 16-byte boundary: the library must fall
     back to the element kernel and still match the oracle bit for bit."""

@@ -30,7 +30,8 @@ STATUS_NAMES = {0: "ZERO_OK", -1: "ZERO_EINVAL", -2: "ZERO_EUNSUPPORTED", -3: "Z
 # Names of every entry point include/zero.h declares.
 ENTRY_POINTS = ("zero_version", "zero_last_error", "zero_plan", "zero_plan_destroy",
                 "zero_plan_info", "zero_plan_bucket", "zero_plan_tensor", "zero_flatten",
-                "zero_shard_reduce", "zero_adam_step", "zero_gather_pack", "zero_reshard")
+                "zero_shard_reduce", "zero_adam_step", "zero_gather_pack", "zero_reshard",
+                "zero_set_write_window")
 
 
 class ZeroError(RuntimeError):
@@ -100,6 +101,8 @@ def load():
     L.zero_gather_pack.argtypes = [vp, ctypes.POINTER(vp), i32, vp, vp]
     L.zero_reshard.restype = i32
     L.zero_reshard.argtypes = [vp, vp, i32, ctypes.POINTER(vp), i32, vp, vp]
+    L.zero_set_write_window.restype = i32
+    L.zero_set_write_window.argtypes = [i64, i64]
     _lib = L
     return L
 
@@ -132,6 +135,16 @@ def _ptr_array(xs) -> ctypes.Array:
 
 def zero_version() -> int:
     return int(load().zero_version())
+
+
+WINDOW_AUTO = -1
+
+
+def zero_set_write_window(period_ticks: int, open_ticks: int = 0) -> None:
+    """Store scheduling of the fused step and the reduction (results are
+    identical): -1 automatic (default), 0 none, else a period of period_ticks
+    real-time-counter ticks (10 ns) whose first open_ticks admit stores."""
+    _check(load().zero_set_write_window(period_ticks, open_ticks))
 
 
 def zero_last_error() -> str:

@@ -13,6 +13,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <new>
 #include <string>
@@ -21,7 +22,7 @@
 #include "zero.h"
 #include "zero_internal.h"
 
-#define ZERO_VERSION_NUMBER 100  // 0.1.0
+#define ZERO_VERSION_NUMBER 101  // 0.1.1
 
 struct zero_plan_s {
   int64_t psi = 0;
@@ -118,6 +119,53 @@ bool pieces_vectorisable(const std::vector<Piece>& ps) {
 
 int ndc_for(int n) { return (n == 4 || n == 8 || n == 16 || n == 64) ? n : 0; }
 
+// Write-window setting: period in the high 32 bits, open ticks in the low 32;
+// kWindowAuto = automatic.  One word, so a reader never sees a torn pair.
+constexpr uint64_t kWindowAuto = ~0ull;
+std::atomic<uint64_t> g_window{kWindowAuto};
+
+// Automatic choice.  A wave waits at most one period, so the period must stay
+// well below the lifetime of a workgroup, or every generation of resident
+// workgroups ends up taking a whole number of periods.  Sweeps on MI355X of
+// the fused step (7.5B at N_d = 64, 13B at N_d = 16, a Stage-3 layer) and of
+// the reduction found the best period near half the time one generation of
+// resident workgroups takes to stream its bytes at ~6.5 TB/s, and the best
+// opening near the written share of the bytes (at least 1/16 of the period).
+// Launches with few ranks per written element or few elements gain nothing.
+constexpr int kAutoMinRanks = 16;
+constexpr int64_t kAutoMinElems = int64_t(1) << 23;
+constexpr double kAutoStreamBps = 6.5e12;
+constexpr double kTickSeconds = 1e-8;   // real-time counter: 100 MHz
+
+void auto_window(int mode, int gdt, int pdt, int ndc, int n_ranks, int64_t elems, int64_t blocks,
+                 zk::StepArgs& a) {
+  if (n_ranks < kAutoMinRanks || elems < kAutoMinElems) return;
+  const int resident = zk::resident_blocks(mode, gdt, pdt, ndc, true);
+  if (resident <= 0 || blocks < 2 * (int64_t)resident) return;
+  const double read = 2.0 * n_ranks + (mode == zk::kFused ? 12.0 : (a.flags & zk::kFlagInitFromOut) ? 4.0 : 0.0);
+  const double written = mode == zk::kFused ? 14.0 : 4.0;
+  const double gen_bytes = (double)resident * zk::kStepThreads * zk::kStepVec * (read + written);
+  double period = gen_bytes / kAutoStreamBps / 2.0 / kTickSeconds;
+  period = std::min<double>(std::max(period, 200.0), (double)zk::kMaxWindowPeriod);
+  const double open = period * std::max(written / (read + written), 1.0 / 16.0);
+  a.win_period = (uint32_t)period;
+  a.win_open = std::max<uint32_t>(1, std::min<uint32_t>((uint32_t)open, a.win_period));
+}
+
+void pick_window(int mode, int gdt, int pdt, int ndc, int n_ranks, int64_t elems, int64_t blocks, bool vec,
+                 zk::StepArgs& a) {
+  a.win_period = 0;
+  a.win_open = 0;
+  if (!vec || mode == zk::kFromReduced) return;
+  const uint64_t w = g_window.load(std::memory_order_relaxed);
+  if (w != kWindowAuto) {
+    a.win_period = (uint32_t)(w >> 32);
+    a.win_open = (uint32_t)w;
+    return;
+  }
+  auto_window(mode, gdt, pdt, ndc, n_ranks, elems, blocks, a);
+}
+
 // Launch the step kernel over all pieces, in chunks of kMaxSeg.
 zero_status run_step(zk::StepArgs& a, const std::vector<Piece>& ps, int mode, int gdt, int pdt,
                      bool vec, void* stream) {
@@ -126,6 +174,7 @@ zero_status run_step(zk::StepArgs& a, const std::vector<Piece>& ps, int mode, in
   while (i < ps.size()) {
     int nseg = 0;
     int64_t blocks = 0;
+    int64_t elems = 0;
     for (; i < ps.size() && nseg < zk::kMaxSeg; ++i) {
       const Piece& q = ps[i];
       const int64_t nb = (q.len + per_block - 1) / per_block;
@@ -137,9 +186,11 @@ zero_status run_step(zk::StepArgs& a, const std::vector<Piece>& ps, int mode, in
       s.len = (int32_t)q.len;
       s.block_start = (int32_t)blocks;
       blocks += nb;
+      elems += q.len;
     }
     a.n_seg = nseg;
     if (blocks == 0) continue;
+    pick_window(mode, gdt, pdt, ndc_for(a.n_ranks), a.n_ranks, elems, blocks, vec, a);
     const int err = zk::launch_step(a, mode, gdt, pdt, ndc_for(a.n_ranks), vec, (int)blocks, stream);
     if (err != 0) return hip_fail(err);
   }
@@ -218,6 +269,20 @@ zero_status run_copies(std::vector<zk::CopyEnt>& ents, void* dst, int es, void* 
 extern "C" {
 
 int32_t zero_version(void) { return ZERO_VERSION_NUMBER; }
+
+zero_status zero_set_write_window(int64_t period_ticks, int64_t open_ticks) {
+  if (period_ticks == -1) {
+    g_window.store(kWindowAuto);
+    return ok();
+  }
+  if (period_ticks < 0 || period_ticks > (int64_t)zk::kMaxWindowPeriod)
+    return fail(ZERO_EINVAL, "period_ticks must be -1 or in [0, %u] (got %lld)", zk::kMaxWindowPeriod,
+                (long long)period_ticks);
+  if (period_ticks > 0 && (open_ticks < 1 || open_ticks > period_ticks))
+    return fail(ZERO_EINVAL, "open_ticks must be in [1, period_ticks] (got %lld)", (long long)open_ticks);
+  g_window.store(period_ticks == 0 ? 0 : ((uint64_t)period_ticks << 32) | (uint64_t)open_ticks);
+  return ok();
+}
 
 const char* zero_last_error(void) { return g_err.c_str(); }
 

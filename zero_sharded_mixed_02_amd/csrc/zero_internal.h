@@ -21,6 +21,14 @@ constexpr int kStepThreads = 512;           // vector step kernel: 8 wave64s (8 
 constexpr int kStepVec = 8;                 // elements per lane in the vector step kernel
 constexpr int kCopyUnits = 4;               // 16-byte units per lane in the copy kernel
 
+// Write windows (vector step kernel, fused and reduce-only modes): a wave that
+// has its results ready waits until the device's real-time counter (a
+// constant 100 MHz clock on gfx950) enters the first win_open ticks of a
+// win_period-tick period, then stores.  Stores of the whole device are thereby
+// gathered into short bursts instead of trickling between the gradient reads.
+constexpr uint32_t kMaxWindowPeriod = 100000;    // 1 ms
+constexpr uint32_t kWindowSpinMax = 1u << 16;    // bound on a wave's wait-loop iterations
+
 // One contiguous piece of the owner's shard (a bucket's slice, or part of it).
 struct StepSeg {
   int64_t shard_off;    // element offset in the shard-local arrays (state, compact grads)
@@ -54,6 +62,8 @@ struct StepArgs {
   int32_t n_ranks;
   int32_t n_seg;
   int32_t flags;
+  uint32_t win_period;    // write window period in real-time-counter ticks; 0 = store at once
+  uint32_t win_open;      // ticks at the start of each period during which waves store
   int32_t pad_;
   StepSeg seg[kMaxSeg];
 };
@@ -82,5 +92,8 @@ int launch_step(const StepArgs& a, int mode, int gdt, int pdt, int ndc, bool vec
                 void* stream);
 int launch_copy(const CopyArgs& a, int esz, int n_blocks, void* stream);
 const char* hip_error_string(int err);
+// Workgroups of the chosen step kernel that the current device holds at once
+// (blocks per CU at the kernel's register use x CUs); 0 if unknown.
+int resident_blocks(int mode, int gdt, int pdt, int ndc, bool vec);
 
 }  // namespace zk

@@ -13,7 +13,8 @@
 //    per rank two 8-byte loads, per fp32 state array two 16-byte loads and
 //    stores, two 8-byte parameter stores.  Every rank pointer and segment
 //    offset is wave-uniform, so address arithmetic stays on the scalar unit
-//    and vector accesses are an SGPR base plus a 32-bit lane offset.
+//    and vector accesses are an SGPR base plus a 32-bit lane offset.  Stores
+//    can be held back to a device-wide write window (see await_write_window).
 //
 //  * copy kernel: destination-aligned 16-byte copies used by flatten (ragged
 //    tensors into padded buckets, at any element offset) and gather_pack
@@ -25,6 +26,8 @@
 // root are HIP's correctly rounded defaults; denormals are preserved.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <atomic>
 
 #include "zero_internal.h"
 
@@ -103,6 +106,36 @@ __device__ __forceinline__ void adam1(const AdamC& k, float g, float& w, float& 
   const float upd = mh / den;
   const float delta = k.lr * upd;
   w = w - delta;
+}
+
+// Keeps the eight values computed before this point: the compiler may not
+// sink their arithmetic (and with it the loads feeding it) below a following
+// wait loop.
+__device__ __forceinline__ void pin8(float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(x[i]));
+}
+
+// Write window.  With period > 0, a wave whose results are ready stores them
+// only while the device's real-time counter is within the first `open` ticks
+// of a `period`-tick period; otherwise it sleeps until the next period begins.
+// The counter is read on the scalar unit, so the branch is wave-uniform.  The
+// wait ends when the counter reaches the target or after kWindowSpinMax
+// iterations, whichever comes first.
+//
+// Why: the step reads ~10 bytes for every byte it writes.  When each wave
+// stores as soon as it is done, writes reach HBM as a thin stream interleaved
+// with the reads, and every read/write turnaround of the DRAM costs far more
+// than the written bytes themselves.  Gathering the stores of all waves into
+// short bursts lets the memory controller drain them together.
+__device__ __forceinline__ void await_write_window(uint32_t period, uint32_t open) {
+  if (period == 0) return;
+  const uint64_t now = __builtin_amdgcn_s_memrealtime();
+  const uint64_t phase = now % period;
+  if (phase < open) return;
+  const uint64_t target = now - phase + period;
+  for (uint32_t i = 0; i < kWindowSpinMax && __builtin_amdgcn_s_memrealtime() < target; ++i)
+    __builtin_amdgcn_s_sleep(4);
 }
 
 // Segment handled by this workgroup (wave-uniform linear scan, <= 64 entries).
@@ -264,6 +297,8 @@ __global__ void __launch_bounds__(kStepThreads) step_vec_kernel(const StepArgs a
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[k] = acc[k] * gs;
     }
+    pin8(acc);
+    await_write_window(a.win_period, a.win_open);
     store_groups(a.out + shard_off, ea, eb, vb, acc);
   }
 
@@ -275,6 +310,10 @@ __global__ void __launch_bounds__(kStepThreads) step_vec_kernel(const StepArgs a
     load_groups(a.v + shard_off, ea, eb, v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) adam1(k, g[i], w[i], m[i], v[i]);
+    pin8(w);
+    pin8(m);
+    pin8(v);
+    await_write_window(a.win_period, a.win_open);
     store_groups(a.master + shard_off, ea, eb, vb, w);
     store_groups(a.m + shard_off, ea, eb, vb, m);
     store_groups(a.v + shard_off, ea, eb, vb, v);
@@ -493,6 +532,28 @@ int launch_copy(const CopyArgs& a, int esz, int n_blocks, void* stream) {
   void* args[] = {(void*)&a};
   return (int)hipLaunchKernel(fn, dim3((unsigned)n_blocks), dim3(kThreads), args, 0,
                               (hipStream_t)stream);
+}
+
+int resident_blocks(int mode, int gdt, int pdt, int ndc, bool vec) {
+  // Cached per kernel variant (all devices this library runs on are the same
+  // gfx950 part); 0 = not yet known, -1 = query failed.
+  static std::atomic<int> cache[3][3][3][5][2];
+  const int ni = ndc == 4 ? 1 : ndc == 8 ? 2 : ndc == 16 ? 3 : ndc == 64 ? 4 : 0;
+  std::atomic<int>& slot = cache[mode % 3][gdt % 3][pdt % 3][ni][vec ? 1 : 0];
+  int r = slot.load(std::memory_order_relaxed);
+  if (r != 0) return r < 0 ? 0 : r;
+  int per_cu = 0, dev = 0, cus = 0;
+  const void* fn = pick_kernel(mode, gdt, pdt, ndc, vec);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, vec ? kStepThreads : kThreads, 0) != hipSuccess ||
+      hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    slot.store(-1, std::memory_order_relaxed);
+    return 0;
+  }
+  r = per_cu * cus;
+  slot.store(r > 0 ? r : -1, std::memory_order_relaxed);
+  return r > 0 ? r : 0;
 }
 
 const char* hip_error_string(int err) { return hipGetErrorString((hipError_t)err); }
