@@ -193,6 +193,13 @@ def measure_kernels(torch):
             t[0] += 1
             run.layer_loop(t[0], pipelined)
         res[name] = _entry(_time_launches(torch, loop, reps=10, warmup=2), pass_bytes, nl * P)
+    # The same pipelined loop with stores issued at once: the side-stream
+    # gathers write continuously, which the step's write window cannot batch.
+    Z.zero_set_write_window(0, 0)
+    res["pipelined_window_off"] = _entry(_time_launches(torch, loop, reps=10, warmup=2), pass_bytes, nl * P)
+    res["serial_window_off"] = _entry(_time_launches(torch, lambda: loop(False), reps=10, warmup=2),
+                                      pass_bytes, nl * P)
+    Z.zero_set_write_window(-1)
     res["speedup"] = res["serial"]["ms"] / res["pipelined"]["ms"]
     res["temp_buffer_bytes"] = {"serial": 2 * P, "pipelined": 4 * P}
     out["stage3_8_layers_h8192_nd64"] = res
