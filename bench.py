@@ -175,6 +175,9 @@ def measure_kernels(torch):
     shards = list(L["shards"])
     out["gather_pack_h8192_nd64"] = _entry(
         _time_launches(torch, lambda: Z.zero_gather_pack(run.plan, shards, Z.ZERO_F16, run.full)), 4 * P, P)
+    # Reference: the runtime's own device copy of the same number of bytes.
+    src = L["shards"].view(-1)[:P]
+    out["torch_copy_same_bytes"] = _entry(_time_launches(torch, lambda: run.full.copy_(src)), 4 * P, P)
 
     def layer_step():
         t[0] += 1

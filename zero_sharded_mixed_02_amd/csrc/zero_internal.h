@@ -19,7 +19,7 @@ constexpr int64_t kSegMaxElems = int64_t(1) << 28;  // keeps per-lane byte offse
 constexpr int kThreads = 256;               // copy and element kernels: 4 wave64s
 constexpr int kStepThreads = 512;           // vector step kernel: 8 wave64s (8 wave tiles)
 constexpr int kStepVec = 8;                 // elements per lane in the vector step kernel
-constexpr int kCopyUnits = 4;               // 16-byte units per lane in the copy kernel
+constexpr int kCopyUnits = 8;               // 16-byte units per lane in the copy kernel
 
 // Write windows (vector step kernel, fused and reduce-only modes): a wave that
 // has its results ready waits until the device's real-time counter (a

@@ -21,6 +21,7 @@
 //    (shards into the full buffer).  A misaligned source is realigned in
 //    registers with byte funnel shifts; partial units at the ends of an entry
 //    are copied element by element, so no byte outside an entry is touched.
+//    Interior workgroups issue all of a lane's loads before its stores.
 //
 // Floating point: compiled with -ffp-contract=off; fp32 division and square
 // root are HIP's correctly rounded defaults; denormals are preserved.
@@ -440,6 +441,47 @@ __global__ void __launch_bounds__(kThreads) copy_kernel(const CopyArgs a) {
       (d0 >> 4) + (uint64_t)(blk - a.ent[ei].block_start) * (kThreads * kCopyUnits);
   const uint64_t s_end = s_begin + (uint64_t)n * ESZ;
   const uint64_t shift = s_begin - d0;   // source byte = destination byte + shift (mod 2^64)
+
+  // Interior workgroups -- every unit a whole 16-byte unit at least 16 bytes
+  // inside the entry -- issue all their loads before any store, so each lane
+  // keeps kCopyUnits loads in flight.  The source misalignment k is the same
+  // for every unit of the entry, so the branches are uniform.
+  constexpr uint64_t kStride = (uint64_t)kThreads * 16;   // bytes between a lane's units
+  const uint64_t blk_lo = ublk << 4;
+  const uint64_t blk_hi = blk_lo + kStride * kCopyUnits;
+  if (blk_lo >= d0 + 16 && blk_hi + 16 <= d1) {
+    const uint64_t ub0 = blk_lo + (uint64_t)threadIdx.x * 16;
+    if (zero_fill) {
+#pragma unroll
+      for (int i = 0; i < kCopyUnits; ++i) st_nt(gaddr<gu32x4*>(ub0 + i * kStride), u32x4{0u, 0u, 0u, 0u});
+      return;
+    }
+    const uint64_t p0 = ub0 + shift;
+    const uint32_t k = (uint32_t)(p0 & 15);
+    if (k == 0) {
+      u32x4 r[kCopyUnits];
+#pragma unroll
+      for (int i = 0; i < kCopyUnits; ++i) r[i] = ld_nt(gaddr<const gu32x4*>(p0 + i * kStride));
+#pragma unroll
+      for (int i = 0; i < kCopyUnits; ++i) st_nt(gaddr<gu32x4*>(ub0 + i * kStride), r[i]);
+    } else {
+      // Both aligned loads of every unit lie inside the source: the unit is
+      // at least 16 bytes from either end of the entry.
+      const uint64_t a0 = p0 - k;
+      u32x4 lo[kCopyUnits], hi[kCopyUnits];
+#pragma unroll
+      for (int i = 0; i < kCopyUnits; ++i) {
+        lo[i] = ld_nt(gaddr<const gu32x4*>(a0 + i * kStride));
+        hi[i] = ld_nt(gaddr<const gu32x4*>(a0 + i * kStride + 16));
+      }
+#pragma unroll
+      for (int i = 0; i < kCopyUnits; ++i)
+        st_nt(gaddr<gu32x4*>(ub0 + i * kStride), funnel(lo[i], hi[i], (int)(k >> 2), k & 3u));
+    }
+    return;
+  }
+
+  // Edge workgroups: unit by unit, partial units element by element.
 #pragma unroll
   for (int i = 0; i < kCopyUnits; ++i) {
     const uint64_t u = ublk + (uint64_t)i * kThreads + threadIdx.x;
