@@ -232,7 +232,7 @@ def measure_kernels(torch):
 # real-time counter) x opening fractions, around the automatic choice.
 WINDOW_GRIDS = {
     "fused_7.5B-stage2": ((3000, 4000, 5000, 6000), (1 / 16, 1 / 11, 1 / 8)),
-    "reduce_7.5B_nd64": ((1000, 1500, 2000, 2500, 3000), (1 / 32, 1 / 16, 1 / 8)),
+    "reduce_7.5B_nd64": ((2000, 3000, 4000, 5000), (1 / 32, 1 / 16, 1 / 8)),
     "fused_13B-stage1": ((1000, 1400, 2000, 2500), (1 / 8, 1 / 4, 3 / 8)),
     "stage3_layer_h8192_nd64": ((3000, 4000, 5000, 6000), (1 / 16, 1 / 8)),
     "fused_gpt2-small": ((500, 1000), (1 / 4, 1 / 2)),

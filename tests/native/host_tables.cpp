@@ -133,9 +133,9 @@ int launch_step(const StepArgs& a, int mode, int gdt, int pdt, int ndc, bool vec
 
 const char* hip_error_string(int) { return "stand-in"; }
 
-// Stand-in occupancy: 4 workgroups per CU for the fused kernel, 2 for the
-// reduce kernel (their register use on gfx950), 256 CUs.
-int resident_blocks(int mode, int, int, int, bool) { return mode == kFused ? 1024 : 512; }
+// Stand-in occupancy: 4 workgroups per CU for the fused kernel, 3 for the
+// reduce kernel (arbitrary; the launcher must use whatever it is told), 256 CUs.
+int resident_blocks(int mode, int, int, int, bool) { return mode == kFused ? 1024 : 768; }
 
 }  // namespace zk
 
@@ -431,11 +431,11 @@ int main() {
                           (float*)(uintptr_t)fake_base(3), (void*)(uintptr_t)fake_base(4), ZERO_F16, 1,
                           nullptr) == ZERO_OK, "large from-reduced step failed: %s", zero_last_error());
     EXPECT(g_steps.size() == 2 && g_steps[1].a.win_period == 0, "window on Adam from the reduced gradient");
-    // The reduction: 512 resident x 4096 x 132 bytes -> 2129 ticks, open 1/16.
+    // The reduction: 768 resident x 4096 x 132 bytes -> 3194 ticks, open 1/16.
     zero_grad_src src16 = {ZERO_BF16, 64, ptrs.data(), nullptr};
     EXPECT(zero_shard_reduce(p, 3, &src16, 1.0 / 64, (float*)(uintptr_t)fake_base(5), nullptr) == ZERO_OK,
            "large reduce failed: %s", zero_last_error());
-    EXPECT(g_steps.size() == 3 && g_steps[2].a.win_period == 2129 && g_steps[2].a.win_open == 133,
+    EXPECT(g_steps.size() == 3 && g_steps[2].a.win_period == 3194 && g_steps[2].a.win_open == 199,
            "automatic window of a large reduce launch: (%u, %u)", g_steps.size() < 3 ? 0u : g_steps[2].a.win_period,
            g_steps.size() < 3 ? 0u : g_steps[2].a.win_open);
     // Few ranks: no automatic window.

@@ -183,12 +183,24 @@ __device__ __forceinline__ void widen4(const u32x2 r, float* x) {
   }
 }
 
+// Ends a batch of the fold: the batch's adds complete before this point and
+// no later load is hoisted above it (the "memory" clobber), so a wave holds
+// one batch of loaded ranks in registers at a time.  Without it the compiler
+// hoists the loads of the whole unrolled rank loop (108 VGPRs for the bf16
+// reduce-only kernel, 172 for fp16), halving or quartering occupancy.
+__device__ __forceinline__ void end_batch(float (&acc)[8]) {
+  asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]),
+               "+v"(acc[6]), "+v"(acc[7])::"memory");
+}
+
 // Fold the launch's ranks for the lane's two 4-element groups (byte offsets
 // boa, bob of each rank's segment base).  acc[0..3] is group a, acc[4..7]
 // group b.  CONT = false: the fold starts from the first rank's value;
 // CONT = true: every rank is added to the incoming acc (continuing a fold
 // begun by an earlier launch).  Loads are issued in batches of B ranks ahead
-// of their adds, so B KiB per wave are in flight; adds keep rank order.
+// of their adds, so B KiB per wave are in flight; adds keep rank order.  fp16
+// batches are 8 ranks: widening fp16 takes more registers than bf16's shifts,
+// and 16 would cost occupancy.
 template <int GDT, int NDC, bool CONT>
 __device__ __forceinline__ void fold(const StepArgs& a, int64_t shard_off, int64_t full_off,
                                      uint32_t boa, uint32_t bob, float (&acc)[8]) {
@@ -200,7 +212,7 @@ __device__ __forceinline__ void fold(const StepArgs& a, int64_t shard_off, int64
     for (int k = 0; k < 8; ++k) acc[k] = first ? x[k] : acc[k] + x[k];
   };
   if constexpr (NDC > 0) {
-    constexpr int B = NDC < 16 ? NDC : 16;
+    constexpr int B = NDC < 16 ? NDC : (GDT == ZERO_F16 ? 8 : 16);
 #pragma unroll
     for (int q0 = 0; q0 < NDC; q0 += B) {
       u32x2 ra[B], rb[B];
@@ -211,6 +223,7 @@ __device__ __forceinline__ void fold(const StepArgs& a, int64_t shard_off, int64
       }
 #pragma unroll
       for (int i = 0; i < B; ++i) take(ra[i], rb[i], !CONT && q0 + i == 0);
+      end_batch(acc);
     }
   } else {
     const int n = a.n_ranks;
@@ -230,6 +243,7 @@ __device__ __forceinline__ void fold(const StepArgs& a, int64_t shard_off, int64
       }
 #pragma unroll
       for (int i = 0; i < B; ++i) take(ra[i], rb[i], false);
+      end_batch(acc);
     }
     for (; q < n; ++q)
       take(ld_nt(grad_pair(a, q, shard_off, full_off, boa)),
