@@ -75,7 +75,22 @@ def cpu_baseline(cfg, n_sample: int):
     dt = time.perf_counter() - t0
     return {"value": n_sample / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n_sample} elements of the owner's shard, {cfg.n_d} "
-                      f"{DTYPE_NAME[cfg.gdt]} slices, one step (t={t_check}); {dt:.2f} s"}
+                      f"{DTYPE_NAME[cfg.gdt]} slices, one step (t={t_check}); {dt:.2f} s",
+            "host": _host_cpu()}
+
+
+def _host_cpu():
+    """CPU model and the logical CPUs this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cpus_available": len(os.sched_getaffinity(0))}
 
 
 def _time_launches(torch, fn, reps=20, warmup=3):
@@ -175,6 +190,13 @@ def measure_kernels(torch):
     shards = list(L["shards"])
     out["gather_pack_h8192_nd64"] = _entry(
         _time_launches(torch, lambda: Z.zero_gather_pack(run.plan, shards, Z.ZERO_F16, run.full)), 4 * P, P)
+    # Calibration: the runtime's own 4 GiB device copy (its copyBuffer
+    # kernel), beside the kernels above.
+    cal_src = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+    cal_dst = torch.empty_like(cal_src)
+    out["calibration_copy_4GiB"] = _entry(_time_launches(torch, lambda: cal_dst.copy_(cal_src), reps=10),
+                                          8 << 30, 1 << 30)
+    del cal_src, cal_dst
     # Reference: the runtime's own device copy of the same number of bytes.
     src = L["shards"].view(-1)[:P]
     out["torch_copy_same_bytes"] = _entry(_time_launches(torch, lambda: run.full.copy_(src)), 4 * P, P)
@@ -225,6 +247,28 @@ def measure_kernels(torch):
         free()
     out["bucket_cap_sweep_gpt2_nd8"] = sweep
     log("bucket sweep done")
+
+    # One plan whose launches cover up to 64 bucket pieces each, against one
+    # plan and one launch per bucket over the same buffers (same results).
+    launches = {}
+    for cap in (1 << 20, 1 << 22, 1 << 24):
+        run = GpuRun(replace(CONFIGS[2], bucket_cap=cap))
+        S = run.S
+        run.fill_grads(1)
+        nb = (2 * 8 + 26) * S
+
+        def per_bucket():
+            t[0] += 1
+            run.step_per_bucket(t[0])
+        e1 = _entry(_time_launches(torch, fused), nb, S)
+        e2 = _entry(_time_launches(torch, per_bucket), nb, S)
+        launches[str(cap)] = {"buckets": run.plan.n_buckets, "one_plan_ms": e1["ms"],
+                              "one_plan_launches": -(-run.plan.n_buckets // 64),
+                              "per_bucket_ms": e2["ms"], "per_bucket_launches": run.plan.n_buckets}
+        del run
+        free()
+    out["multi_bucket_launch_gpt2_nd8"] = launches
+    log("launch-count comparison done")
     return out
 
 

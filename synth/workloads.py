@@ -252,6 +252,53 @@ class GpuRun:
             stepped[layer].record(main)
         main.wait_stream(side)
 
+    def bucket_plans(self):
+        """One plan per bucket of this run's plan, over that bucket's tensors
+        alone, with the slices of this run's buffers that the bucket owns:
+        (plan, shard_off, flat_off) per bucket.  Padding is per bucket, so the
+        bucket's own plan lays it out exactly as the whole plan does."""
+        if getattr(self, "_bucket_plans", None) is None:
+            Z, cfg = self.Z, self.cfg
+            per = [[] for _ in self.buckets]
+            for t, n in enumerate(cfg.sizes):
+                per[self.plan.tensor(t)[0]].append(n)
+            self._bucket_plans = []
+            for b, (flat_off, numel, padded, sn, shard_off) in enumerate(self.buckets):
+                bp = Z.zero_plan(numel, cfg.n_d, per[b], 0, cfg.align)
+                if bp.psi_pad != padded or bp.shard_total != sn:
+                    raise AssertionError(f"bucket {b}: own plan has a different layout")
+                self._bucket_plans.append((bp, shard_off, flat_off))
+        return self._bucket_plans
+
+    def _bucket_calls(self, layer: int):
+        """Per bucket: (plan, gradient source, master, m, v, destination
+        addresses, destination is full), built once per layer."""
+        cache = self.__dict__.setdefault("_bucket_calls_cache", {})
+        if layer not in cache:
+            cfg, L, Z = self.cfg, self.layers[layer], self.Z
+            g_es, p_es = ESIZE[cfg.gdt], ESIZE[cfg.pdt]
+            calls = []
+            for bp, soff, foff in self.bucket_plans():
+                ptrs = [L["grads"][q].data_ptr() + (foff if q in cfg.full_ranks else soff) * g_es
+                        for q in range(cfg.n_d)]
+                src = Z.GradSrc(cfg.gdt, ptrs, [1 if q in cfg.full_ranks else 0 for q in range(cfg.n_d)])
+                if cfg.stage == 3:
+                    dst, dst_full = L["shards"][cfg.owner].data_ptr() + soff * p_es, False
+                else:
+                    dst, dst_full = self.full.data_ptr() + foff * p_es, True
+                calls.append((bp, src, L["master"].data_ptr() + soff * 4, L["m"].data_ptr() + soff * 4,
+                              L["v"].data_ptr() + soff * 4, dst, dst_full))
+            cache[layer] = calls
+        return cache[layer]
+
+    def step_per_bucket(self, t: int, layer: int = 0, stream=None):
+        """The step as one zero_adam_step call (one launch) per bucket, each
+        with the bucket's own plan and pointers into this run's buffers."""
+        cfg, Z = self.cfg, self.Z
+        for bp, src, w, m, v, dst, dst_full in self._bucket_calls(layer):
+            Z.zero_adam_step(bp, cfg.owner, cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.grad_scale, t, src,
+                             None, w, m, v, dst, cfg.pdt, dst_full, stream)
+
     def reduce(self, out, layer: int = 0, stream=None):
         self.Z.zero_shard_reduce(self.plan, self.cfg.owner, self.src[layer], self.cfg.grad_scale, out, stream)
 

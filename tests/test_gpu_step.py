@@ -120,6 +120,28 @@ def test_fused_equals_unfused(gpu, oracle_lib, name):
     assert np.array_equal(a["full"], b["full"])
 
 
+@pytest.mark.parametrize("name", ["multibucket-nd4", "manybuckets-nd4-align8", "stage1-nd5-somefull", "gpt2"])
+def test_per_bucket_plans_equal_one_plan(gpu, name):
+    """A step as one zero_adam_step per bucket, each with a plan of that
+    bucket's tensors alone and pointers into the same buffers, equals the
+    step with the whole multi-bucket plan, bit for bit (the concept page's
+    trade-off 1: buckets are independent units of the step)."""
+    cfg = CONFIGS[2] if name == "gpt2" else SMALL_CASES[name]
+    say(f"[per-bucket plans] {name}: {len(cfg.sizes)} tensors")
+    whole, split = GpuRun(cfg), GpuRun(cfg)
+    assert len(split.bucket_plans()) == whole.plan.n_buckets
+    for t in (1, 2):
+        whole.fill_grads(t)
+        split.fill_grads(t)
+        whole.step(t)
+        split.step_per_bucket(t)
+    _sync()
+    a, b = whole.fetch(), split.fetch()
+    for k in ("master", "m", "v"):
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
+    assert np.array_equal(a["full"], b["full"])
+
+
 def test_reduce_more_ranks_than_one_launch(gpu, oracle_lib):
     """n_d = 200 > ZERO_MAX_RANKS: the reduction continues across launches in
     rank order; the fused path refuses, the reduced path is exact."""
