@@ -34,6 +34,8 @@ def test_memory_table1_closed_form(oracle_lib):
     mem = O.memory_closed_form(psi, n_d, k)
     for stage in ("dp", "os", "os_g", "os_g_p"):
         assert f"{mem[stage] / 1e9:.1f}" == g[stage], stage
+    # The default K is the concept page's 12 bytes of fp32 optimizer state.
+    assert O.memory_closed_form(psi, n_d) == mem
 
 
 @pytest.mark.parametrize("align", [1, 64])
@@ -145,11 +147,17 @@ def test_plan_bruteforce_invariants(oracle_lib):
         for t, n in enumerate(sizes):
             bk = p.buckets[p.tensor_bucket[t]]
             assert bk.flat_off <= p.tensor_off[t] and p.tensor_off[t] + n <= bk.flat_off + bk.numel
-        # Greedy cap rule.
+        # Greedy cap rule: a bucket holding several tensors stays within the
+        # cap, and every bucket but the last was closed only because its
+        # successor's first tensor would have taken it past the cap (a bucket
+        # may be filled exactly to the cap).
         for b, bk in enumerate(p.buckets):
             members = [t for t in range(len(sizes)) if p.tensor_bucket[t] == b]
             if cap and len(members) > 1:
                 assert bk.numel <= cap
+            if cap and b + 1 < len(p.buckets):
+                first_next = min(t for t in range(len(sizes)) if p.tensor_bucket[t] == b + 1)
+                assert bk.numel + sizes[first_next] > cap
         # flatten / unflatten round trip, pads zero.
         rng = np.random.default_rng(psi)
         ts = [rng.integers(1, 2 ** 16, size=n, dtype=np.uint16) for n in sizes]
@@ -400,6 +408,72 @@ def test_adam_accuracy_against_fp64(oracle_lib):
         # the bound is a few ulps of the largest term per step.
         assert np.all(np.abs(m32 - m64) <= t * 2.0 ** -22 * np.abs(g).max())
         assert np.all(np.abs(v32 - v64) <= t * 2.0 ** -22 * np.abs(v64).max())
+
+
+def _adam_f32_sequence(c, g, w, m, v):
+    """The stated update, each binary operation evaluated by numpy in IEEE
+    binary32 (one rounding per operation, no fused multiply-add)."""
+    f = np.float32
+    b1, c1, b2, c2, bc1, bc2, lr, eps = (f(x) for x in c[:8])
+    mn = f(b1 * m) + f(c1 * g)
+    vn = f(b2 * v) + f(c2 * f(g * g))
+    den = f(np.sqrt(f(vn / bc2))) + eps
+    wn = w - f(lr * f(f(mn / bc1) / den))
+    return f(wn), f(mn), f(vn)
+
+
+def _fma32(a, b, c):
+    """fp32 fused multiply-add: the product of two fp32 values is exact in
+    fp64, so a*b + c rounded once to fp64 and then to fp32 (double rounding
+    is possible only at rare ties; enough to show the inputs are sensitive)."""
+    return np.float32(np.float64(a) * np.float64(b) + np.float64(c))
+
+
+def test_adam_one_rounding_per_operation(oracle_lib):
+    """The oracle rounds after every operation of the update and fuses none:
+    on inputs where contracting any multiply-add of the rule (b1*m + c1*g,
+    b2*v + c2*g^2, w - lr*r) changes the fp32 result, it equals the
+    operation-by-operation binary32 evaluation bit for bit."""
+    O = oracle_lib
+    rng = np.random.default_rng(21)
+    n = 4096
+    g = rng.normal(0, 1e-3, n).astype(np.float32)
+    w = rng.normal(0, 0.02, n).astype(np.float32)
+    m = rng.normal(0, 1e-4, n).astype(np.float32)
+    v = np.abs(rng.normal(0, 1e-7, n)).astype(np.float32)
+    c = O.adam_consts(LR, B1, B2, EPS, 1.0, 7)
+    ww, mm, vv = w.copy(), m.copy(), v.copy()
+    O.adam(g, ww, mm, vv, c, O.F16)
+    want = [_adam_f32_sequence(c, g[i], w[i], m[i], v[i]) for i in range(n)]
+    got = list(zip(ww, mm, vv))
+    assert all(np.float32(a).view(np.uint32) == np.float32(b).view(np.uint32)
+               for gw, ww_ in zip(got, want) for a, b in zip(gw, ww_))
+    # The inputs have teeth: each contraction changes some results.
+    f = np.float32
+    fused_m = sum(_fma32(c[0], m[i], f(c[1] * g[i])) != want[i][1] for i in range(n))
+    fused_v = sum(_fma32(c[2], v[i], f(c[3] * f(g[i] * g[i]))) != want[i][2] for i in range(n))
+    fused_w = 0
+    for i in range(n):
+        den = f(np.sqrt(f(want[i][2] / c[5]))) + c[7]
+        r = f(f(want[i][1] / c[4]) / den)
+        fused_w += _fma32(-c[6], r, w[i]) != want[i][0]
+    assert fused_m > 0 and fused_v > 0 and fused_w > 0, (fused_m, fused_v, fused_w)
+
+
+def test_decode16_exhaustive(oracle_lib):
+    """Every 16-bit pattern decodes to its IEEE value: binary16 against
+    numpy's float16, bfloat16 against the fp32 whose upper half it is."""
+    O = oracle_lib
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = O.value16(h, O.F16)
+    want = h.view(np.float16).astype(np.float64)
+    assert np.array_equal(got, want, equal_nan=True)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+    got = O.value16(h, O.BF16)
+    with np.errstate(invalid="ignore"):     # signalling-NaN patterns widen quietly
+        want = (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.array_equal(got, want, equal_nan=True)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
 
 
 def test_adam_param_is_rounded_master(oracle_lib):
