@@ -250,6 +250,7 @@ zero_status run_copies(std::vector<zk::CopyEnt>& ents, void* dst, int es, void* 
       const uint64_t d1 = d0 + (uint64_t)e.n * es;
       const int64_t units = (int64_t)(((d1 + 15) >> 4) - (d0 >> 4));
       const int64_t nb = (units + units_per_block - 1) / units_per_block;
+      if (nb > INT32_MAX) return fail(ZERO_EINVAL, "copy of %lld elements exceeds one launch", (long long)e.n);
       if (blocks + nb > INT32_MAX) break;
       a.ent[n] = e;
       a.ent[n].block_start = (int32_t)blocks;
