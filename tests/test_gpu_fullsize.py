@@ -56,6 +56,37 @@ def test_stage12_full_size(gpu, oracle_lib, num):
     _free(run)
 
 
+def test_unfused_full_size(gpu, oracle_lib):
+    """The 7.5B, N_d = 64 workload through zero_shard_reduce (its automatic
+    write window included) and zero_adam_step from the reduced gradient: the
+    sampled reduced gradient and state equal the oracle's."""
+    import torch
+    import oracle as O
+    from oracle.runner import OracleRun
+    from tests.parity import assert_f32
+    cfg = CONFIGS[3]
+    say(f"[full size, unfused] config 3 {cfg.name}: psi={cfg.psi} n_d={cfg.n_d}, 2 steps")
+    run = GpuRun(cfg)
+    J = sample_indices(run.S, seed=33)
+    ref = OracleRun(cfg, sample=J)
+    red = torch.empty(run.S, dtype=torch.float32, device=gpu)
+    j_t = torch.from_numpy(J).to(gpu)
+    for t in (1, 2):
+        run.fill_grads(t)
+        ref.fill_grads(t)
+        run.reduce(red)
+        run.step_from_reduced(t, red)
+        ref.step(t)
+        torch.cuda.synchronize()
+        want = O.reduce(ref.layers[0]["slices"], cfg.gdt, float(np.float32(cfg.grad_scale)))
+        assert_f32(red[j_t].cpu().numpy(), want, "reduced", bitwise=True)
+        say(f"  step {t} done")
+    r = assert_state(run.fetch_at(J, ref.pos), ref.state(), cfg.pdt, cfg.name)
+    say(f"  sample of {J.size}: {r}")
+    del red
+    _free(run)
+
+
 def test_stage3_full_size(gpu, oracle_lib):
     import torch
     import synth
