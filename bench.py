@@ -455,6 +455,21 @@ def main():
 
     launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     total_ms = starts[0].elapsed_time(ends[-1])
+
+    # Outside the timed region: a few steps each right after a fresh 15 GB
+    # gradient fill (plain stores), timed one by one.  A long write-only phase
+    # just before the step costs it most of its write-window gain.
+    fresh_ms = []
+    for _ in range(4):
+        t += 1
+        run.fill_grads(t)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run.step(t)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fresh_ms.append(e0.elapsed_time(e1))
     ms_per_step = total_ms / args.steps
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
     bpp = algorithmic_bytes_per_param(cfg.n_d)
@@ -486,6 +501,9 @@ def main():
                      "algorithmic_bytes_per_launch": launch_bytes,
                      "avg_launch_ms": avg_launch_s * 1e3, "kernel": "step_vec_kernel (fused)"},
         "write_window": "automatic (library default)",
+        "after_fresh_gradient_fill": {
+            "ms_per_step": sum(fresh_ms) / len(fresh_ms), "steps": len(fresh_ms),
+            "note": "not the timed region: each step right after a 15 GB plain-store refill of the gradients"},
     }
     del run
     torch.cuda.synchronize()
