@@ -438,6 +438,22 @@ int main() {
     EXPECT(g_steps.size() == 3 && g_steps[2].a.win_period == 3194 && g_steps[2].a.win_open == 199,
            "automatic window of a large reduce launch: (%u, %u)", g_steps.size() < 3 ? 0u : g_steps[2].a.win_period,
            g_steps.size() < 3 ? 0u : g_steps[2].a.win_open);
+    // Three generations of resident workgroups (3 x 1024 x 4096 elements):
+    // half the period, 2484 ticks, open 225.
+    {
+      std::vector<int64_t> s3 = {(int64_t)3 * 1024 * 4096 * 64};
+      zero_plan_t p3;
+      zero_plan(s3[0], 64, s3.data(), 1, 0, 64, &p3);
+      g_steps.clear();
+      EXPECT(zero_adam_step(p3, 1, &hp, 1, &src, nullptr, (float*)(uintptr_t)fake_base(1),
+                            (float*)(uintptr_t)fake_base(2), (float*)(uintptr_t)fake_base(3),
+                            (void*)(uintptr_t)fake_base(4), ZERO_F16, 1, nullptr) == ZERO_OK,
+             "3-generation step failed: %s", zero_last_error());
+      EXPECT(g_steps.size() == 1 && g_steps[0].a.win_period == 2484 && g_steps[0].a.win_open == 225,
+             "automatic window of a 3-generation launch: (%u, %u)", g_steps.empty() ? 0u : g_steps[0].a.win_period,
+             g_steps.empty() ? 0u : g_steps[0].a.win_open);
+      zero_plan_destroy(p3);
+    }
     // Few ranks: no automatic window.
     std::vector<int64_t> s8 = {((int64_t)1 << 25) * 8};
     zero_plan_t p8;

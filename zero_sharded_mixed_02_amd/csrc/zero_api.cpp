@@ -132,7 +132,11 @@ std::atomic<uint64_t> g_window{kWindowAuto};
 // resident workgroups takes to stream its bytes at ~6.5 TB/s, and the best
 // opening near the written share of the bytes (at least 1/16 of the period).
 // Launches with few ranks per written element or few elements gain nothing.
+// A launch of only a few generations (a Stage-3 layer is three) does better
+// with a proportionally shorter period: its waits at the end are not hidden
+// by later generations.
 constexpr int kAutoMinRanks = 16;
+constexpr double kAutoFullGenerations = 6.0;
 constexpr int64_t kAutoMinElems = int64_t(1) << 23;
 constexpr double kAutoStreamBps = 6.5e12;
 constexpr double kTickSeconds = 1e-8;   // real-time counter: 100 MHz
@@ -146,6 +150,7 @@ void auto_window(int mode, int gdt, int pdt, int ndc, int n_ranks, int64_t elems
   const double written = mode == zk::kFused ? 14.0 : 4.0;
   const double gen_bytes = (double)resident * zk::kStepThreads * zk::kStepVec * (read + written);
   double period = gen_bytes / kAutoStreamBps / 2.0 / kTickSeconds;
+  period *= std::min(1.0, (double)blocks / resident / kAutoFullGenerations);
   period = std::min<double>(std::max(period, 200.0), (double)zk::kMaxWindowPeriod);
   const double open = period * std::max(written / (read + written), 1.0 / 16.0);
   a.win_period = (uint32_t)period;
