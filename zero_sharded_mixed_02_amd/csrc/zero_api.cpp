@@ -203,7 +203,7 @@ zero_status run_step(zk::StepArgs& a, const std::vector<Piece>& ps, int mode, in
 }
 
 // Fill the rank table of a step launch with ranks [q0, q0 + n).
-void set_ranks(zk::StepArgs& a, const zero_plan_s& p, const zero_grad_src& src, int q0, int n) {
+void set_ranks(zk::StepArgs& a, const zero_grad_src& src, int q0, int n) {
   memset(a.grad, 0, sizeof a.grad);
   memset(a.full_mask, 0, sizeof a.full_mask);
   for (int i = 0; i < n; ++i) {
@@ -211,7 +211,6 @@ void set_ranks(zk::StepArgs& a, const zero_plan_s& p, const zero_grad_src& src, 
     if (src.is_full && src.is_full[q0 + i]) a.full_mask[i >> 5] |= 1u << (i & 31);
   }
   a.n_ranks = n;
-  (void)p;
 }
 
 // Common checks of a gradient source; collects the read ranges.
@@ -531,7 +530,7 @@ zero_status zero_shard_reduce(zero_plan_t p, int32_t rank, const zero_grad_src* 
     // Ranks beyond one launch's table: later launches continue from out.
     for (int q0 = 0; q0 < p->n_d; q0 += zk::kMaxRanks) {
       const int n = std::min(zk::kMaxRanks, p->n_d - q0);
-      set_ranks(a, *p, *src, q0, n);
+      set_ranks(a, *src, q0, n);
       a.flags = (q0 > 0 ? zk::kFlagInitFromOut : 0) | (q0 + n == p->n_d ? zk::kFlagApplyScale : 0);
       if (zero_status st = run_step(a, ps, zk::kReduceOnly, src->dtype, ZERO_F16, vec, stream)) return st;
     }
@@ -599,7 +598,7 @@ zero_status zero_adam_step(zero_plan_t p, int32_t rank, const zero_adam_hyper* h
     a.v = v;
     a.dst = param_dst;
     if (slices) {
-      set_ranks(a, *p, *slices, 0, p->n_d);
+      set_ranks(a, *slices, 0, p->n_d);
       return run_step(a, ps, zk::kFused, slices->dtype, param_dt, vec, stream);
     }
     a.reduced = reduced;
