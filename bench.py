@@ -14,7 +14,7 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
              counter summary when it was taken on the current kernel source
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 7.5B-stage2]
 """
 import argparse
 import hashlib
@@ -117,15 +117,17 @@ def _entry(ms, nbytes, elems):
 
 
 def measure_kernels(torch):
-    """Every entry point at its own workload (see the design doc for the byte
-    counts): fused step on the 7.5B, 13B and GPT-2 workloads, the unfused
-    reduce and Adam-from-reduced on 7.5B, flatten of the GPT-2 tensor list,
-    and the Stage-3 layer (gather_pack, then fused step)."""
+    """Every entry point at its own workload: fused step on the 7.5B, 13B and
+    GPT-2 workloads, the unfused reduce and Adam-from-reduced on 7.5B, flatten
+    of the GPT-2 tensor list, and the Stage-3 layer (gather_pack, then fused
+    step).  Algorithmic bytes per element: fused 2 N_d + 26, reduce 2 N_d + 4,
+    Adam from the reduced gradient 30, flatten 4 per real and 2 per pad
+    element, gather_pack 4."""
     import zero_sharded_mixed_02_amd as Z
     import synth
     from synth import gpu as SG
     from dataclasses import replace
-    from synth.workloads import CONFIGS, GpuRun, gpt2_small_sizes
+    from synth.workloads import WORKLOADS, GpuRun, gpt2_small_sizes
     out = {}
 
     def free():
@@ -133,7 +135,7 @@ def measure_kernels(torch):
         torch.cuda.empty_cache()
 
     # 7.5B, N_d = 64: fused, and the two unfused halves.
-    cfg = CONFIGS[3]
+    cfg = WORKLOADS["7.5B-stage2"]
     run = GpuRun(cfg)
     S = run.S
     run.fill_grads(1)
@@ -155,7 +157,7 @@ def measure_kernels(torch):
     log("7.5B kernels done")
 
     # 13B Stage 1, N_d = 16 (owner's full buffer + 15 owned slices).
-    run = GpuRun(CONFIGS[4])
+    run = GpuRun(WORKLOADS["13B-stage1"])
     S = run.S
     run.fill_grads(1)
     out["fused_13B_stage1_nd16"] = _entry(_time_launches(torch, fused, reps=10), (2 * 16 + 26) * S, S)
@@ -164,7 +166,7 @@ def measure_kernels(torch):
     log("13B kernels done")
 
     # GPT-2-small list, N_d = 8, 7 buckets (partly cache-resident).
-    run = GpuRun(CONFIGS[2])
+    run = GpuRun(WORKLOADS["gpt2-small"])
     S = run.S
     run.fill_grads(1)
     out["fused_gpt2_nd8"] = _entry(_time_launches(torch, fused), (2 * 8 + 26) * S, S)
@@ -183,7 +185,7 @@ def measure_kernels(torch):
     log("GPT-2 kernels done")
 
     # Stage 3: one h = 8192 layer, N_d = 64 (gather_pack, then the fused step).
-    run = GpuRun(CONFIGS[5])
+    run = GpuRun(WORKLOADS["stage3-h8192x8"])
     S, P = run.S, run.P
     run.fill_grads(1, 0)
     L = run.layers[0]
@@ -236,7 +238,7 @@ def measure_kernels(torch):
     # 64 shard pieces; more buckets mean more launches).
     sweep = {}
     for cap in (1 << 18, 1 << 20, 1 << 22, 1 << 24, 1 << 26, 0):
-        run = GpuRun(replace(CONFIGS[2], bucket_cap=cap))
+        run = GpuRun(replace(WORKLOADS["gpt2-small"], bucket_cap=cap))
         S = run.S
         run.fill_grads(1)
         e = _entry(_time_launches(torch, fused), (2 * 8 + 26) * S, S)
@@ -252,7 +254,7 @@ def measure_kernels(torch):
     # plan and one launch per bucket over the same buffers (same results).
     launches = {}
     for cap in (1 << 20, 1 << 22, 1 << 24):
-        run = GpuRun(replace(CONFIGS[2], bucket_cap=cap))
+        run = GpuRun(replace(WORKLOADS["gpt2-small"], bucket_cap=cap))
         S = run.S
         run.fill_grads(1)
         nb = (2 * 8 + 26) * S
@@ -290,7 +292,7 @@ def measure_windows(torch):
     7.5B reduce-only launch.  Results are bit-identical under every setting;
     only the store timing changes."""
     import zero_sharded_mixed_02_amd as Z
-    from synth.workloads import CONFIGS, GpuRun
+    from synth.workloads import WORKLOADS, GpuRun
     t = [0]
     out = {}
 
@@ -319,16 +321,16 @@ def measure_windows(torch):
                 run.step(t[0], layer)
         return f
 
-    for num, reps in ((3, 10), (4, 4), (5, 10), (2, 20)):
-        run = GpuRun(CONFIGS[num])
+    for name, reps in (("7.5B-stage2", 10), ("13B-stage1", 4), ("stage3-h8192x8", 10), ("gpt2-small", 20)):
+        run = GpuRun(WORKLOADS[name])
         n_d, S = run.cfg.n_d, run.S
-        if num == 5:
+        if run.cfg.stage == 3:
             run.fill_grads(1, 0)
             sweep("stage3_layer_h8192_nd64", fused_of(run, 0), 4 * run.P + (2 * n_d + 26) * S, run.P, reps)
         else:
             run.fill_grads(1)
             sweep(f"fused_{run.cfg.name}", fused_of(run), (2 * n_d + 26) * S, S, reps)
-        if num == 3:
+        if name == "7.5B-stage2":
             red = torch.empty(S, dtype=torch.float32, device="cuda")
             sweep("reduce_7.5B_nd64", lambda: run.reduce(red), (2 * n_d + 4) * S, S, reps)
             del red
@@ -392,7 +394,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--workload", default="7.5B-stage2",
+                    help="workload name (synth.workloads.WORKLOADS); Stage 1/2 only")
     ap.add_argument("--cpu-sample", type=int, default=1 << 24)
     ap.add_argument("--copy-probe", action="store_true",
                     help="time a plain 4 GiB device copy (calibrates HBM byte counters)")
@@ -417,13 +420,15 @@ def main():
     if args.copy_probe:
         copy_probe(torch)
         return
-    from synth.workloads import CONFIGS, GpuRun
+    from synth.workloads import WORKLOADS, GpuRun
     from __graft_entry__ import _ensure_built
     _ensure_built()
 
-    cfg = CONFIGS[args.workload]
+    if args.workload not in WORKLOADS:
+        raise SystemExit(f"unknown workload {args.workload!r}; one of {sorted(WORKLOADS)}")
+    cfg = WORKLOADS[args.workload]
     if cfg.stage == 3:
-        raise SystemExit("bench.py times the Stage-1/2 fused step; workload 5 is a parity case")
+        raise SystemExit("bench.py times the Stage-1/2 fused step; the Stage-3 workload is a parity case")
     torch.cuda.init()
     log(f"setting up {cfg.name}: psi={cfg.psi} n_d={cfg.n_d}")
     run = GpuRun(cfg)

@@ -1,24 +1,24 @@
 """The workloads of the shard step and their GPU-side set-up.
 
-``CONFIGS`` holds the five workloads by number; ``GpuRun`` allocates one
+``WORKLOADS`` holds the five workloads by name; ``GpuRun`` allocates one
 workload's buffers on the GPU, fills them with the seeded inputs of
 synth/__init__.py (through libsynth.so) and drives the C ABI of libzero.so.
 This module holds no arithmetic of the step: inputs here are generated, and
 every step of the path runs in libzero.so's kernels.
 
-Workload shapes (stand-ins for the models on the ZeRO pages):
-  1 tiny        flat 1,000,003 params, N_d=4, fp16 grads and params, 3 steps
-  2 gpt2-small  193-tensor GPT-2-small list (h=768, 12 layers, 50257-row
+Workload shapes (stand-ins for the models on the ZeRO pages), by name:
+  tiny          flat 1,000,003 params, N_d=4, fp16 grads and params, 3 steps
+  gpt2-small    193-tensor GPT-2-small list (h=768, 12 layers, 50257-row
                 embedding), N_d=8, bf16 grads and params, 2^24-element
                 buckets, 10 steps
-  3 7.5B        flat 7.5e9 params, N_d=64, Stage 2 (compact bf16 slices, full
+  7.5B-stage2   flat 7.5e9 params, N_d=64, Stage 2 (compact bf16 slices, full
                 fp16 param buffer), 6 steps (5 warm-up + the checked one);
                 the paper's Table 1 model (mind-map page, "Stage 1/2/3")
-  4 13B         flat 13e9 params, N_d=16, Stage 1 (the owner's full fp16
+  13B-stage1    flat 13e9 params, N_d=16, Stage 1 (the owner's full fp16
                 gradient buffer plus the peers' owned slices), zero/outlier
                 gradient mix, 5 steps; the size the abstract quotes as
                 trainable without model parallelism
-  5 stage3      one h=8192 transformer layer (805,412,864 params) x 8 layers,
+  stage3-h8192x8  one h=8192 transformer layer (805,412,864 params) x 8 layers,
                 N_d=64, fp16 resident shards, bf16 grads; per layer
                 gather_pack then the fused step (concept page, "three stages")
 """
@@ -86,14 +86,14 @@ class Config:
         return 1.0 / self.n_d
 
 
-CONFIGS = {
-    1: Config("tiny", (1_000_003,), n_d=4, gdt=F16, pdt=F16, steps=3, seed=1),
-    2: Config("gpt2-small", tuple(gpt2_small_sizes()), n_d=8, gdt=BF16, pdt=BF16,
+WORKLOADS = {
+    "tiny": Config("tiny", (1_000_003,), n_d=4, gdt=F16, pdt=F16, steps=3, seed=1),
+    "gpt2-small": Config("gpt2-small", tuple(gpt2_small_sizes()), n_d=8, gdt=BF16, pdt=BF16,
               bucket_cap=1 << 24, steps=10, seed=2),
-    3: Config("7.5B-stage2", (7_500_000_000,), n_d=64, gdt=BF16, pdt=F16, steps=6, seed=3),
-    4: Config("13B-stage1", (13_000_000_000,), n_d=16, gdt=F16, pdt=F16, stage=1, steps=5,
+    "7.5B-stage2": Config("7.5B-stage2", (7_500_000_000,), n_d=64, gdt=BF16, pdt=F16, steps=6, seed=3),
+    "13B-stage1": Config("13B-stage1", (13_000_000_000,), n_d=16, gdt=F16, pdt=F16, stage=1, steps=5,
               seed=4, mix=True, full_ranks=(0,)),
-    5: Config("stage3-h8192x8", tuple(layer_sizes(8192)), n_d=64, gdt=BF16, pdt=F16, stage=3,
+    "stage3-h8192x8": Config("stage3-h8192x8", tuple(layer_sizes(8192)), n_d=64, gdt=BF16, pdt=F16, stage=3,
               steps=1, layers=8, seed=5),
 }
 

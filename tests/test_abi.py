@@ -57,10 +57,10 @@ def test_plan_matches_oracle_bruteforce(zero_lib, oracle_lib):
         assert lp.n_d == n_d
 
 
-@pytest.mark.parametrize("num", [1, 2, 3, 4, 5])
-def test_plan_matches_oracle_workloads(zero_lib, oracle_lib, num):
-    from synth.workloads import CONFIGS
-    c = CONFIGS[num]
+@pytest.mark.parametrize("name", ["tiny", "gpt2-small", "7.5B-stage2", "13B-stage1", "stage3-h8192x8"])
+def test_plan_matches_oracle_workloads(zero_lib, oracle_lib, name):
+    from synth.workloads import WORKLOADS
+    c = WORKLOADS[name]
     lp = zero_lib.zero_plan(c.psi, c.n_d, list(c.sizes), c.bucket_cap, c.align)
     op = oracle_lib.plan(c.psi, c.n_d, list(c.sizes), c.bucket_cap, c.align)
     assert _plan_tuple_lib(zero_lib, lp, len(c.sizes)) == _plan_tuple_oracle(op)

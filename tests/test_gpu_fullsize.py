@@ -6,7 +6,7 @@ elementwise in the shard index."""
 import numpy as np
 import pytest
 
-from synth.workloads import CONFIGS, GpuRun
+from synth.workloads import WORKLOADS, GpuRun
 from tests.parity import assert_p16, assert_state
 
 pytestmark = [pytest.mark.gpu, pytest.mark.big]
@@ -33,15 +33,15 @@ def _free(run):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("num", [3, 4])
-def test_stage12_full_size(gpu, oracle_lib, num):
+@pytest.mark.parametrize("name", ["7.5B-stage2", "13B-stage1"])
+def test_stage12_full_size(gpu, oracle_lib, name):
     import torch
     from oracle.runner import OracleRun
-    cfg = CONFIGS[num]
-    say(f"[full size] config {num} {cfg.name}: psi={cfg.psi} n_d={cfg.n_d} steps={cfg.steps}")
+    cfg = WORKLOADS[name]
+    say(f"[full size] {cfg.name}: psi={cfg.psi} n_d={cfg.n_d} steps={cfg.steps}")
     run = GpuRun(cfg)
     say(f"  resident {run.bytes_resident() / 1e9:.1f} GB, S={run.S}")
-    J = sample_indices(run.S, seed=num)
+    J = sample_indices(run.S, seed=cfg.seed)
     ref = OracleRun(cfg, sample=J)
     for t in range(1, cfg.steps + 1):
         run.fill_grads(t)
@@ -64,8 +64,8 @@ def test_unfused_full_size(gpu, oracle_lib):
     import oracle as O
     from oracle.runner import OracleRun
     from tests.parity import assert_f32
-    cfg = CONFIGS[3]
-    say(f"[full size, unfused] config 3 {cfg.name}: psi={cfg.psi} n_d={cfg.n_d}, 2 steps")
+    cfg = WORKLOADS["7.5B-stage2"]
+    say(f"[full size, unfused] {cfg.name}: psi={cfg.psi} n_d={cfg.n_d}, 2 steps")
     run = GpuRun(cfg)
     J = sample_indices(run.S, seed=33)
     ref = OracleRun(cfg, sample=J)
@@ -91,11 +91,11 @@ def test_stage3_full_size(gpu, oracle_lib):
     import torch
     import synth
     from oracle.runner import OracleRun
-    cfg = CONFIGS[5]
-    say(f"[full size] config 5 {cfg.name}: {cfg.layers} layers of {cfg.psi} params, n_d={cfg.n_d}")
+    cfg = WORKLOADS["stage3-h8192x8"]
+    say(f"[full size] {cfg.name}: {cfg.layers} layers of {cfg.psi} params, n_d={cfg.n_d}")
     run = GpuRun(cfg)
     say(f"  resident {run.bytes_resident() / 1e9:.1f} GB, S={run.S}")
-    J = sample_indices(run.S, seed=5)
+    J = sample_indices(run.S, seed=cfg.seed)
     ref = OracleRun(cfg, sample=J)
     rng = np.random.default_rng(55)
     flat_sample = np.unique(np.concatenate([np.arange(4096), np.arange(run.P - 4096, run.P),

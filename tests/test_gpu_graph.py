@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 from synth import BF16, F16
-from synth.workloads import CONFIGS, GpuRun, small_config
+from synth.workloads import WORKLOADS, GpuRun, small_config
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +40,7 @@ def test_graph_replays_match_eager(gpu, zero_lib, case, window):
     if case == "nd64":
         cfg = small_config(300_000, 64, BF16, F16, owner=5, steps=1, seed=41)
     else:
-        cfg = replace(CONFIGS[5], sizes=(96, 96, 8192), n_d=8, owner=3, layers=2, seed=42)
+        cfg = replace(WORKLOADS["stage3-h8192x8"], sizes=(96, 96, 8192), n_d=8, owner=3, layers=2, seed=42)
     say(f"[graph] {case} window={window}")
     if window:
         Z.zero_set_write_window(*window)

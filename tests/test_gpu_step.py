@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 from synth import BF16, F16, F32
-from synth.workloads import CONFIGS, Config, GpuRun, small_config, with_owner
+from synth.workloads import WORKLOADS, Config, GpuRun, small_config, with_owner
 from tests.parity import assert_f32, assert_p16, assert_state
 
 pytestmark = pytest.mark.gpu
@@ -26,10 +26,10 @@ def _sync():
 
 
 SMALL_CASES = {
-    "tiny-owner0": CONFIGS[1],
-    "tiny-owner3-pad": with_owner(CONFIGS[1], 3),
-    "tiny-bf16-owner2": replace(CONFIGS[1], gdt=BF16, pdt=BF16, owner=2),
-    "tiny-align1-elem": replace(CONFIGS[1], align=1, owner=3),
+    "tiny-owner0": WORKLOADS["tiny"],
+    "tiny-owner3-pad": with_owner(WORKLOADS["tiny"], 3),
+    "tiny-bf16-owner2": replace(WORKLOADS["tiny"], gdt=BF16, pdt=BF16, owner=2),
+    "tiny-align1-elem": replace(WORKLOADS["tiny"], align=1, owner=3),
     "nd3-generic": small_config(77_777, 3, BF16, F16, owner=1, steps=2, seed=7),
     "nd1": small_config(50_001, 1, F16, BF16, owner=0, steps=2, seed=8),
     "nd64-lastrank": small_config(300_000, 64, BF16, F16, owner=63, steps=2, seed=9),
@@ -68,14 +68,14 @@ def test_fused_step_matches_oracle(gpu, oracle_lib, name):
 
 
 def test_large_step_numbers(gpu, oracle_lib):
-    cfg = replace(CONFIGS[1], steps=3)
+    cfg = replace(WORKLOADS["tiny"], steps=3)
     say("[fused step] tiny at t = 998, 999, 1000")
     run, ref = run_pair(cfg, t_values=[998, 999, 1000])
     assert_state(run.fetch(), ref.state(), cfg.pdt, "t~1000")
 
 
 def test_gpt2_small_ten_steps(gpu, oracle_lib):
-    cfg = CONFIGS[2]
+    cfg = WORKLOADS["gpt2-small"]
     say(f"[fused step] gpt2-small: {len(cfg.sizes)} tensors, n_d={cfg.n_d}, 10 steps")
     run, ref = run_pair(cfg)
     got, want = run.fetch(), ref.state()
@@ -85,7 +85,7 @@ def test_gpt2_small_ten_steps(gpu, oracle_lib):
 
 def test_gpt2_small_every_owner_one_step(gpu, oracle_lib):
     for owner in range(8):
-        cfg = with_owner(replace(CONFIGS[2], steps=1), owner)
+        cfg = with_owner(replace(WORKLOADS["gpt2-small"], steps=1), owner)
         say(f"[fused step] gpt2-small owner {owner}")
         run, ref = run_pair(cfg)
         assert_state(run.fetch(), ref.state(), cfg.pdt, f"gpt2 owner {owner}")
@@ -126,7 +126,7 @@ def test_per_bucket_plans_equal_one_plan(gpu, name):
     bucket's tensors alone and pointers into the same buffers, equals the
     step with the whole multi-bucket plan, bit for bit (the concept page's
     trade-off 1: buckets are independent units of the step)."""
-    cfg = CONFIGS[2] if name == "gpt2" else SMALL_CASES[name]
+    cfg = WORKLOADS["gpt2-small"] if name == "gpt2" else SMALL_CASES[name]
     say(f"[per-bucket plans] {name}: {len(cfg.sizes)} tensors")
     whole, split = GpuRun(cfg), GpuRun(cfg)
     assert len(split.bucket_plans()) == whole.plan.n_buckets
