@@ -63,20 +63,45 @@ def measured_traffic(launch_bytes: float):
 
 
 def cpu_baseline(cfg, n_sample: int):
-    """The oracle (single-threaded C) on a contiguous sample of the shard."""
+    """The oracle (single-threaded C) on a contiguous sample of the shard; then
+    the same inputs split into contiguous ranges, one thread each (every
+    operation is elementwise, so the results are the same bits)."""
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle as O
     from oracle.runner import OracleRun
     J = np.arange(n_sample, dtype=np.int64)
     ref = OracleRun(cfg, sample=J)
     t_check = cfg.steps
     ref.fill_grads(t_check)
+    L = ref.layers[0]
+    w0, m0, v0 = L["master"].copy(), L["m"].copy(), L["v"].copy()
     t0 = time.perf_counter()
     ref.step(t_check)
     dt = time.perf_counter() - t0
-    return {"value": n_sample / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n_sample} elements of the owner's shard, {cfg.n_d} "
-                      f"{DTYPE_NAME[cfg.gdt]} slices, one step (t={t_check}); {dt:.2f} s",
-            "host": _host_cpu()}
+    out = {"value": n_sample / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+           "sample": f"first {n_sample} elements of the owner's shard, {cfg.n_d} "
+                     f"{DTYPE_NAME[cfg.gdt]} slices, one step (t={t_check}); {dt:.2f} s",
+           "host": _host_cpu()}
+    ncpu = min(16, len(os.sched_getaffinity(0)))
+    if ncpu > 1:
+        cut = np.linspace(0, n_sample, ncpu + 1).astype(np.int64)
+        parts = [(lo, hi, w0[lo:hi].copy(), m0[lo:hi].copy(), v0[lo:hi].copy())
+                 for lo, hi in zip(cut[:-1], cut[1:])]
+
+        def one(part):
+            lo, hi, w, m, v = part
+            O.shard_step([sl[lo:hi] for sl in L["slices"]], cfg.gdt, ref.hp, t_check, w, m, v, cfg.pdt)
+
+        with ThreadPoolExecutor(ncpu) as ex:   # the oracle's C calls release the GIL
+            t0 = time.perf_counter()
+            list(ex.map(one, parts))
+            dt_all = time.perf_counter() - t0
+        same = all(np.array_equal(np.concatenate([p[i] for p in parts]).view(np.uint32), L[k].view(np.uint32))
+                   for i, k in ((2, "master"), (3, "m"), (4, "v")))
+        out["all_cores"] = {"value": n_sample / dt_all, "unit": "params/s", "cores": ncpu,
+                            "seconds": dt_all, "same_bits_as_one_thread": bool(same)}
+    return out
 
 
 def _host_cpu():
