@@ -255,6 +255,13 @@ def measure_kernels(torch):
     res["speedup"] = res["serial"]["ms"] / res["pipelined"]["ms"]
     res["temp_buffer_bytes"] = {"serial": 2 * P, "pipelined": 4 * P}
     out["stage3_8_layers_h8192_nd64"] = res
+
+    # The same loop with a stand-in for each layer's compute between its
+    # gather and its step: the six weight GEMMs of a transformer layer's
+    # forward (q, k, v, output, MLP in and out) on 2048 tokens, fp16, reading
+    # the gathered weights.  Prefetching layer l+1 on the side stream can now
+    # hide behind layer l's compute.
+    out["stage3_8_layers_with_compute"] = _stage3_with_compute(torch, run, t, nl, P, S)
     del run, shards, L
     free()
     log("Stage-3 kernels done")
@@ -363,6 +370,46 @@ def measure_windows(torch):
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
     return out
+
+
+def _stage3_with_compute(torch, run, t, nl, P, S, tokens=2048):
+    import zero_sharded_mixed_02_amd as Z
+    h = 8192
+    offs = [run.plan.tensor(i)[1] for i in range(len(run.cfg.sizes))]
+    x = (torch.randn(tokens, h, device="cuda") * 0.5).to(torch.float16)
+
+    def w(buf, i, r, c):
+        return buf[offs[i]:offs[i] + r * c].view(torch.float16).view(r, c)
+
+    def compute(layer, buf):
+        q = x @ w(buf, 2, h, h)
+        x @ w(buf, 4, h, h)
+        x @ w(buf, 6, h, h)
+        q @ w(buf, 8, h, h)
+        hid = x @ w(buf, 12, h, 4 * h)
+        hid @ w(buf, 14, 4 * h, h)
+
+    def compute_only():
+        for layer in range(nl):
+            compute(layer, run.full)
+
+    flops = nl * 2 * tokens * 12 * h * h
+    res = {"tokens": tokens, "compute_tflop_per_pass": flops / 1e12}
+    res["compute_only_ms"] = _time_launches(torch, compute_only, reps=5, warmup=2)
+    res["gather_only_ms"] = nl * _time_launches(
+        torch, lambda: Z.zero_gather_pack(run.plan, list(run.layers[0]["shards"]), run.cfg.pdt, run.full),
+        reps=10, warmup=2)
+    for name, pipelined, window in (("serial", False, -1), ("pipelined", True, -1),
+                                    ("pipelined_window_off", True, 0)):
+        Z.zero_set_write_window(window, 0)
+
+        def loop(pipelined=pipelined):
+            t[0] += 1
+            run.layer_loop(t[0], pipelined, compute)
+        res[name + "_ms"] = _time_launches(torch, loop, reps=5, warmup=2)
+    Z.zero_set_write_window(-1)
+    res["gather_hidden_fraction"] = (res["serial_ms"] - res["pipelined_ms"]) / res["gather_only_ms"]
+    return res
 
 
 def _counter_means(path, kernel_substr, counter):

@@ -197,17 +197,23 @@ class GpuRun:
                                       cfg.mix, ks)
 
     # -- the path -------------------------------------------------------------
-    def step(self, t: int, layer: int = 0, stream=None):
+    def step(self, t: int, layer: int = 0, stream=None, compute=None):
+        """The path for one layer.  Stage 3: gather_pack into the full-layer
+        buffer, then compute(layer, buffer) if given (a stand-in for the
+        layer's forward and backward, which read the gathered weights), then
+        the fused step into the owner's resident shard."""
         cfg, L, Z = self.cfg, self.layers[layer], self.Z
         if cfg.stage == 3:
             Z.zero_gather_pack(self.plan, list(L["shards"]), cfg.pdt, self.full, stream)
+            if compute is not None:
+                compute(layer, self.full)
             dst, dst_full = L["shards"][cfg.owner], False
         else:
             dst, dst_full = self.full, True
         Z.zero_adam_step(self.plan, cfg.owner, cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.grad_scale, t,
                          self.src[layer], None, L["master"], L["m"], L["v"], dst, cfg.pdt, dst_full, stream)
 
-    def layer_loop(self, t: int, pipelined: bool = False):
+    def layer_loop(self, t: int, pipelined: bool = False, compute=None):
         """One Stage-3 pass over all layers: for each layer, gather_pack of
         the layer's shards into a full-layer buffer, then the fused step into
         the owner's resident shard.
@@ -217,11 +223,13 @@ class GpuRun:
         buffers, so gather(l+1) overlaps step(l).  Events keep the order the
         serial loop has: step(l) starts after gather(l) has read the owner's
         pre-step shard, and gather(l+2) reuses a buffer only after step(l)
-        (standing in for the layer's compute that reads it) has finished."""
+        (standing in for the layer's compute that reads it) has finished.
+        compute(layer, buffer), if given, runs on the current stream between a
+        layer's gather and its step, reading the gathered buffer."""
         torch, Z, cfg = self.torch, self.Z, self.cfg
         if not pipelined:
             for layer in range(cfg.layers):
-                self.step(t, layer)
+                self.step(t, layer, compute=compute)
             return
         if getattr(self, "full2", None) is None:
             self.full2 = torch.zeros_like(self.full)
@@ -245,6 +253,8 @@ class GpuRun:
             if layer + 1 < cfg.layers:
                 gather(layer + 1)
             main.wait_event(gathered[layer])
+            if compute is not None:
+                compute(layer, bufs[layer % 2])
             L = self.layers[layer]
             Z.zero_adam_step(self.plan, cfg.owner, cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.grad_scale, t,
                              self.src[layer], None, L["master"], L["m"], L["v"], L["shards"][cfg.owner],

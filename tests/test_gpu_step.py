@@ -318,6 +318,44 @@ def test_stage3_pipelined_loop_matches_serial(gpu, oracle_lib):
         assert np.array_equal(bufs[prev % 2], ref.state(prev)["gathered"])
 
 
+def test_stage3_compute_sees_its_layer(gpu, oracle_lib):
+    """With a layer compute between gather and step, every layer's compute
+    reads exactly that layer's gathered weights (the pre-step shards), in the
+    serial loop and in the prefetching two-stream loop, where the gather of
+    layer l+1 runs during layer l's compute and step."""
+    import torch
+    from oracle.runner import OracleRun
+    from synth.workloads import layer_sizes
+    cfg = Config("stage3-compute", tuple(layer_sizes(128)), n_d=8, gdt=BF16, pdt=F16, stage=3,
+                 owner=2, steps=2, layers=5, seed=29)
+    say("[stage3] compute between gather and step, h=128 n_d=8 layers=5 steps=2")
+    serial, pipe, ref = GpuRun(cfg), GpuRun(cfg), OracleRun(cfg)
+    seen = {name: [torch.empty_like(serial.full) for _ in range(cfg.layers)] for name in ("serial", "pipe")}
+
+    def recorder(name):
+        def compute(layer, buf):
+            seen[name][layer].copy_(buf)       # what this layer's compute read
+        return compute
+
+    for t in range(1, cfg.steps + 1):
+        for layer in range(cfg.layers):
+            serial.fill_grads(t, layer)
+            pipe.fill_grads(t, layer)
+            ref.fill_grads(t, layer)
+        serial.layer_loop(t, pipelined=False, compute=recorder("serial"))
+        pipe.layer_loop(t, pipelined=True, compute=recorder("pipe"))
+        for layer in range(cfg.layers):
+            ref.step(t, layer)
+        _sync()
+        for layer in range(cfg.layers):
+            want = ref.state(layer)["gathered"]
+            for name in ("serial", "pipe"):
+                got = seen[name][layer].cpu().numpy().view(np.uint16)
+                assert np.array_equal(got, want), (t, layer, name)
+            a, b = serial.fetch(layer), pipe.fetch(layer)
+            assert np.array_equal(a["shards"], b["shards"]), (t, layer)
+
+
 # ---------------------------------------------------------------------------
 # Special values and the output conversion
 # ---------------------------------------------------------------------------
