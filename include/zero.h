@@ -165,7 +165,9 @@ ZERO_API zero_status zero_flatten(zero_plan_t plan, const void* const* tensors, 
  *   src    the n_d contributions (see zero_grad_src).
  *   out    device fp32 buffer of shard_total elements (shard-local layout).
  * Any n_d is supported (ranks beyond ZERO_MAX_RANKS are folded by further
- * launches that continue from `out`, which keeps the same order).
+ * launches that continue from `out`, which keeps the same order).  Stores may
+ * be held for a device-wide write window (zero_set_write_window); the result
+ * never depends on it.
  * Errors: EINVAL for a bad rank, src->n != n_d, nulls, misalignment, out
  * overlapping a gradient buffer; EUNSUPPORTED for a non-16-bit dtype.
  */
@@ -200,6 +202,8 @@ ZERO_API zero_status zero_shard_reduce(zero_plan_t plan, int32_t rank, const zer
  *               dst_is_full == 0: the rank's resident parameter shard
  *               (shard_total elements, Stage 3).
  *   param_dt    ZERO_F16 or ZERO_BF16.
+ * With slices, the kernel may hold its stores for a device-wide write window
+ * (zero_set_write_window); the results never depend on it.
  * Errors: EINVAL for a bad rank, t < 1, nulls, misalignment, src->n != n_d,
  * overlapping outputs; EUNSUPPORTED for non-16-bit types or for the fused
  * path with n_d > ZERO_MAX_RANKS (use zero_shard_reduce, then reduced).
