@@ -1,5 +1,5 @@
-"""The host launch tables of libzero, checked on the CPU under
-AddressSanitizer and UndefinedBehaviorSanitizer.
+"""The host launch tables of libzero, and the CPU oracle's C code, checked
+on the CPU under AddressSanitizer and UndefinedBehaviorSanitizer.
 
 tests/native/host_tables.cpp is compiled with the library's host code
 (zero_api.cpp) in place of the HIP launchers.  Its stand-in launchers replay
@@ -39,3 +39,19 @@ def test_host_launch_tables(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "0 failures" in r.stdout
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+def test_oracle_under_sanitizers(tmp_path):
+    """The CPU oracle's C entry points on edge inputs (zero counts, 1 and 130
+    ranks, every 16-bit pattern decoded, a strided fp32 sweep encoded,
+    NaN/Inf/denormal Adam inputs) under AddressSanitizer and UBSan."""
+    exe = tmp_path / "oracle_sanitize"
+    cmd = ["gcc", "-std=c11", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-Wall", "-Wextra", "-Werror", os.path.join(ROOT, "tests", "native", "oracle_sanitize.c"),
+           os.path.join(ROOT, "oracle", "zero_oracle.c"), "-o", str(exe), "-lm"]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:verify_asan_link_order=0")
+    r = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "oracle sanitize ok" in r.stdout
