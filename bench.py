@@ -449,6 +449,71 @@ def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     print(json.dumps(rec))
 
 
+# Kernels run by --counter-run, each by one workload only: kernel-name
+# fragment -> (workload, elements per dispatch key, algorithmic bytes per element).
+COUNTER_KERNELS = {
+    "step_vec_kernel<0, 2, 1, 64>": ("fused step, 7.5B, N_d=64", "S_7.5B", 2 * 64 + 26),
+    "step_vec_kernel<2, 2, 1, 64>": ("reduce, 7.5B, N_d=64", "S_7.5B", 2 * 64 + 4),
+    "step_vec_kernel<1, 2, 1, 1>": ("Adam from reduced, 7.5B", "S_7.5B", 4 + 24 + 2),
+    "step_vec_kernel<0, 1, 1, 16>": ("fused step, 13B Stage 1, N_d=16", "S_13B", 2 * 16 + 26),
+    "copy_kernel<2>": ("gather_pack, h=8192 layer, N_d=64", "P_stage3", 4),
+}
+
+
+def counter_run(torch):
+    """Each entry point on its workload, twice, for rocprofv3 --pmc runs (no
+    timing).  Prints the element counts the counter table divides by."""
+    from synth.workloads import WORKLOADS, GpuRun
+    sizes = {}
+    run = GpuRun(WORKLOADS["7.5B-stage2"])
+    sizes["S_7.5B"] = run.S
+    red = torch.empty(run.S, dtype=torch.float32, device="cuda")
+    for t in (1, 2):
+        run.fill_grads(t)
+        run.step(t)
+        run.reduce(red)
+        run.step_from_reduced(t + 2, red)
+        torch.cuda.synchronize()
+    del run, red
+    torch.cuda.empty_cache()
+    run = GpuRun(WORKLOADS["13B-stage1"])
+    sizes["S_13B"] = run.S
+    for t in (1, 2):
+        run.fill_grads(t)
+        run.step(t)
+        torch.cuda.synchronize()
+    del run
+    torch.cuda.empty_cache()
+    import zero_sharded_mixed_02_amd as Z
+    run = GpuRun(WORKLOADS["stage3-h8192x8"])
+    sizes["P_stage3"] = run.P
+    for _ in range(2):
+        Z.zero_gather_pack(run.plan, list(run.layers[0]["shards"]), run.cfg.pdt, run.full)
+        torch.cuda.synchronize()
+    print(json.dumps({"counter_run": sizes}))
+
+
+def write_counter_table(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, sizes_json, out_md):
+    """HBM bytes per element of every kernel of --counter-run, from FETCH_SIZE
+    and WRITE_SIZE (KiB per dispatch), scaled by the copy probe's counters."""
+    copy_bytes = 4 << 30
+    cf, _ = _counter_means(copy_fetch_csv, "copyBuffer", "FETCH_SIZE")
+    cw, _ = _counter_means(copy_write_csv, "copyBuffer", "WRITE_SIZE")
+    kf, kw = cf * 1024 / copy_bytes, cw * 1024 / copy_bytes
+    sizes = json.loads(open(sizes_json).read().strip().splitlines()[-1])["counter_run"]
+    rows = []
+    for frag, (what, key, alg) in COUNTER_KERNELS.items():
+        f, nf = _counter_means(fetch_csv, frag, "FETCH_SIZE")
+        w, nw = _counter_means(write_csv, frag, "WRITE_SIZE")
+        n = sizes[key]
+        rd, wr = f * 1024 / kf / n, w * 1024 / kw / n
+        rows.append(f"| {what} | `{frag}` | {nf}/{nw} | {rd:.2f} | {wr:.2f} | {rd + wr:.2f} | {alg} |")
+    with open(out_md, "w") as fh:
+        fh.write("| workload | kernel | dispatches (fetch/write) | read B/elem | written B/elem | "
+                 "total | algorithmic |\n|---|---|---|---|---|---|---|\n" + "\n".join(rows) + "\n")
+    print("\n".join(rows))
+
+
 def copy_probe(torch):
     """A plain device copy of known size, for scaling rocprofv3's FETCH_SIZE and
     WRITE_SIZE counters to bytes: each dispatch reads and writes 4 GiB."""
@@ -469,6 +534,11 @@ def main():
     ap.add_argument("--workload", default="7.5B-stage2",
                     help="workload name (synth.workloads.WORKLOADS); Stage 1/2 only")
     ap.add_argument("--cpu-sample", type=int, default=1 << 24)
+    ap.add_argument("--counter-run", action="store_true",
+                    help="run each entry point on its workload twice for rocprofv3 --pmc runs and exit")
+    ap.add_argument("--write-counter-table", nargs=6,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "SIZES_JSON", "OUT_MD"),
+                    help="summarise --counter-run counter CSVs into a bytes-per-element table and exit")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time a plain 4 GiB device copy (calibrates HBM byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -482,6 +552,9 @@ def main():
     if args.write_traffic:
         write_traffic(*args.write_traffic)
         return
+    if args.write_counter_table:
+        write_counter_table(*args.write_counter_table)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the step is one rank's share, and its "
               "throughput at N GPUs is N times the one-GPU figure with no collective in the path; "
@@ -489,6 +562,11 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.counter_run:
+        from __graft_entry__ import _ensure_built
+        _ensure_built()
+        counter_run(torch)
+        return
     if args.copy_probe:
         copy_probe(torch)
         return
