@@ -55,3 +55,22 @@ def test_oracle_under_sanitizers(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "oracle sanitize ok" in r.stdout
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
+def test_host_code_thread_safety(tmp_path):
+    """libzero's host code from eight threads at once (own and shared plans,
+    every entry point, per-thread error text) while another thread changes
+    the write-window setting, under ThreadSanitizer."""
+    exe = tmp_path / "host_threads"
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=thread", "-Wall", "-Werror",
+           "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(ROOT, "zero_sharded_mixed_02_amd", "csrc"),
+           os.path.join(ROOT, "tests", "native", "host_threads.cpp"),
+           os.path.join(ROOT, "zero_sharded_mixed_02_amd", "csrc", "zero_api.cpp"),
+           "-o", str(exe), "-pthread"]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1:exitcode=66")
+    r = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "0 failures" in r.stdout
