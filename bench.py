@@ -15,6 +15,7 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 7.5B-stage2]
+       [--owner R] [--shard-align A] [--bucket-cap C]
 """
 import argparse
 import hashlib
@@ -533,6 +534,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="7.5B-stage2",
                     help="workload name (synth.workloads.WORKLOADS); Stage 1/2 only")
+    ap.add_argument("--owner", type=int, default=None, help="owning rank (default: the workload's)")
+    ap.add_argument("--shard-align", type=int, default=None, help="shard alignment in elements")
+    ap.add_argument("--bucket-cap", type=int, default=None, help="bucket cap in elements (0 = one bucket)")
     ap.add_argument("--cpu-sample", type=int, default=1 << 24)
     ap.add_argument("--counter-run", action="store_true",
                     help="run each entry point on its workload twice for rocprofv3 --pmc runs and exit")
@@ -577,6 +581,16 @@ def main():
     if args.workload not in WORKLOADS:
         raise SystemExit(f"unknown workload {args.workload!r}; one of {sorted(WORKLOADS)}")
     cfg = WORKLOADS[args.workload]
+    from dataclasses import replace
+    from synth.workloads import with_owner
+    if args.owner is not None:
+        if not 0 <= args.owner < cfg.n_d:
+            raise SystemExit(f"--owner must be in [0, {cfg.n_d})")
+        cfg = with_owner(cfg, args.owner)
+    if args.shard_align is not None:
+        cfg = replace(cfg, align=args.shard_align)
+    if args.bucket_cap is not None:
+        cfg = replace(cfg, bucket_cap=args.bucket_cap)
     if cfg.stage == 3:
         raise SystemExit("bench.py times the Stage-1/2 fused step; the Stage-3 workload is a parity case")
     torch.cuda.init()
@@ -646,6 +660,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": cfg.name, "psi": cfg.psi, "n_d": cfg.n_d, "owner": cfg.owner,
+                   "shard_align": cfg.align, "bucket_cap": cfg.bucket_cap,
                    "shard_params": S, "grad_dtype": DTYPE_NAME[cfg.gdt],
                    "param_dtype": DTYPE_NAME[cfg.pdt], "stage": cfg.stage},
         "hbm_gbps": launch_bytes / (ms_per_step / 1e3) / 1e9,

@@ -105,9 +105,17 @@ std::vector<StepRec> g_steps;
 }  // namespace
 
 // ---- stand-ins for the launchers: replay the kernels' indexing ----------
+// When set, the next launch "fails" with this HIP error code.
+int g_inject_error = 0;
+
 namespace zk {
 
 int launch_copy(const CopyArgs& a, int esz, int n_blocks, void*) {
+  if (g_inject_error) {
+    const int e = g_inject_error;
+    g_inject_error = 0;
+    return e;
+  }
   // Entry of each block: last entry whose block_start <= block.
   for (int e = 0; e < a.n_ent; ++e) {
     const CopyEnt& en = a.ent[e];
@@ -127,11 +135,16 @@ int launch_copy(const CopyArgs& a, int esz, int n_blocks, void*) {
 }
 
 int launch_step(const StepArgs& a, int mode, int gdt, int pdt, int ndc, bool vec, int n_blocks, void*) {
+  if (g_inject_error) {
+    const int e = g_inject_error;
+    g_inject_error = 0;
+    return e;
+  }
   g_steps.push_back(StepRec{a, mode, gdt, pdt, ndc, n_blocks, vec});
   return 0;
 }
 
-const char* hip_error_string(int) { return "stand-in"; }
+const char* hip_error_string(int) { return "stand-in launch error"; }
 
 // Stand-in occupancy: 4 workgroups per CU for the fused kernel, 3 for the
 // reduce kernel (arbitrary; the launcher must use whatever it is told), 256 CUs.
@@ -386,6 +399,37 @@ int main() {
     zero_plan_destroy(p);
     ++cases;
     (void)q;
+  }
+  // A failed launch surfaces as ZERO_EHIP with the runtime's message, from
+  // the step, the reduction and the copies alike.
+  {
+    std::vector<int64_t> sizes = {5000, 3000};
+    zero_plan_t p;
+    zero_plan(8000, 4, sizes.data(), 2, 0, 8, &p);
+    const PlanQ q = query(p);
+    std::vector<const void*> ptrs(4);
+    for (int r = 0; r < 4; ++r) ptrs[r] = (const void*)(uintptr_t)fake_base(100 + r);
+    zero_grad_src src = {ZERO_BF16, 4, ptrs.data(), nullptr};
+    zero_adam_hyper hp = {1e-4, 0.9, 0.999, 1e-8, 0.25};
+    g_inject_error = 700;
+    EXPECT(zero_adam_step(p, 1, &hp, 1, &src, nullptr, (float*)(uintptr_t)fake_base(1),
+                          (float*)(uintptr_t)fake_base(2), (float*)(uintptr_t)fake_base(3),
+                          (void*)(uintptr_t)fake_base(4), ZERO_F16, 1, nullptr) == ZERO_EHIP,
+           "step launch error not reported");
+    EXPECT(strstr(zero_last_error(), "stand-in launch error") && strstr(zero_last_error(), "700"),
+           "step launch error text: %s", zero_last_error());
+    g_inject_error = 701;
+    EXPECT(zero_shard_reduce(p, 0, &src, 0.25, (float*)(uintptr_t)fake_base(5), nullptr) == ZERO_EHIP,
+           "reduce launch error not reported");
+    std::vector<const void*> sh(4);
+    for (int r = 0; r < 4; ++r) sh[r] = (const void*)(uintptr_t)fake_base(300 + r);
+    g_inject_error = 702;
+    EXPECT(zero_gather_pack(p, sh.data(), ZERO_BF16, (void*)(uintptr_t)fake_base(6), nullptr) == ZERO_EHIP,
+           "copy launch error not reported");
+    EXPECT(strstr(zero_last_error(), "702") != nullptr, "copy launch error text: %s", zero_last_error());
+    EXPECT(g_inject_error == 0, "error not consumed");
+    (void)q;
+    zero_plan_destroy(p);
   }
   // Write-window setting: range checks, forced values reach every fused and
   // reduce launch, and -1 restores the automatic choice.
