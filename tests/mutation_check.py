@@ -15,6 +15,7 @@ R = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 BASE = None
 C = 'oracle/zero_oracle.c'
 P = 'oracle/__init__.py'
+RUN = 'oracle/runner.py'
 MUTANTS = [
     # (name, file, old, new)
     ("reduce: start from +0", C, "float acc = orc_widen(slices[0], dt, j);\n        for (int32_t q = 1;", "float acc = 0.0f;\n        for (int32_t q = 0;"),
@@ -55,6 +56,8 @@ MUTANTS = [
     ("volume: stage 3 one gather", P, '        ops = {"reduce_scatter": walk(), "all_gather_fwd": walk(), "all_gather_bwd": walk()}', '        ops = {"reduce_scatter": walk(), "all_gather_fwd": walk()}'),
     ("volume: self slice dropped", P, "                total += hi - lo\n", "                total += (hi - lo) if r != perspective else 0\n"),
     ("reshard: source rank 0 only", P, "    full = gather_pack(src, src_shards)\n", "    full = gather_pack(src, [src_shards[0]] * len(src_shards))\n"),
+    ("stage3: gather after the step", RUN, "        if self.cfg.stage == 3 and self.sample is None:\n            L[\"gathered\"] = gather_pack(self.plan, L[\"shards\"])\n        L[\"params\"] = shard_step(L[\"slices\"], self.cfg.gdt, self.hp, t, L[\"master\"], L[\"m\"], L[\"v\"],\n                                 self.cfg.pdt)\n        if self.cfg.stage == 3 and self.sample is None:\n            L[\"shards\"][self.cfg.owner] = L[\"params\"]\n", "        L[\"params\"] = shard_step(L[\"slices\"], self.cfg.gdt, self.hp, t, L[\"master\"], L[\"m\"], L[\"v\"],\n                                 self.cfg.pdt)\n        if self.cfg.stage == 3 and self.sample is None:\n            L[\"shards\"][self.cfg.owner] = L[\"params\"]\n            L[\"gathered\"] = gather_pack(self.plan, L[\"shards\"])\n"),
+    ("stage3: owner shard not replaced", RUN, "            L[\"shards\"][self.cfg.owner] = L[\"params\"]\n", "            pass\n"),
     ("f64 adam: eps inside", C, "w[j] = w[j] - lr * mhat / (sqrt(vhat) + eps);", "w[j] = w[j] - lr * mhat / sqrt(vhat + eps);"),
 ]
 

@@ -573,3 +573,63 @@ def test_reshard_invariants(oracle_lib):
         same = [O.reshard(src, src, r, shards) for r in range(n_d)]
         for a, b in zip(same, shards):
             assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# Stage 3: the per-layer sequence (gather the pre-step shards, step, the owner
+# keeps its new 16-bit shard for the next gather)
+# ---------------------------------------------------------------------------
+
+def _stage3_expected_full(O, cfg, p, layer):
+    """The full layer as every rank holds it before any step: the
+    round-to-nearest-even 16-bit value of each initial master weight, zero in
+    the padding.  Computed from the input definition and numpy's float16
+    conversion, without the oracle's gather or its casts."""
+    import synth
+    pos = np.arange(p.psi_pad, dtype=np.int64)
+    pad = np.zeros(p.psi_pad, bool)
+    for bk in p.buckets:
+        pad[bk.flat_off + bk.numel: bk.flat_off + bk.padded] = True
+    w0 = synth.master_values(cfg.seed, pos + layer * p.psi_pad, cfg.sigma_w, pad)
+    return w0.astype(np.float16).view(np.uint16)
+
+
+def test_stage3_sequence(oracle_lib):
+    """The oracle's Stage-3 layer step follows the pages' order (mind-map
+    page, how a GPU that keeps a quarter computes: the layer's parameters are
+    gathered for the computation, then the owner updates its part and keeps
+    it; concept page, "three stages" table, Stage-3 row: parameters are
+    gathered per layer and only the owner's shard stays resident).  Over three
+    layers and two steps, with an owner other than rank 0 and several buckets:
+    each layer's gathered buffer equals the layer as the shards stood before
+    that layer's step -- at t = 1 the rounded initial masters, at t = 2 the
+    same with the owner's block replaced by step 1's parameters -- the owner's
+    shard after every step is the rounding of its master, and no other shard
+    ever changes."""
+    from oracle.runner import OracleRun
+    from synth.workloads import Config, layer_sizes
+    O = oracle_lib
+    cfg = Config("stage3-tiny", tuple(layer_sizes(8)), n_d=4, gdt=O.BF16, pdt=O.F16, stage=3,
+                 owner=2, bucket_cap=200, align=8, steps=2, layers=3, seed=9)
+    run = OracleRun(cfg)
+    p = run.plan
+    assert len(p.buckets) > 1 and cfg.owner != 0
+    expected = [_stage3_expected_full(O, cfg, p, layer) for layer in range(cfg.layers)]
+    owner_pos = np.concatenate([np.arange(*p.owner_range(b, cfg.owner)) for b in range(len(p.buckets))])
+    others0 = [[run.layers[layer]["shards"][q].copy() for q in range(cfg.n_d)] for layer in range(cfg.layers)]
+    for t in (1, 2):
+        for layer in range(cfg.layers):
+            run.fill_grads(t, layer)
+            run.step(t, layer)
+            st = run.state(layer)
+            assert np.array_equal(st["gathered"], expected[layer]), (t, layer)
+            rounded = st["master"].astype(np.float16).view(np.uint16)
+            assert np.array_equal(st["shards"][cfg.owner], rounded), (t, layer)
+            for q in range(cfg.n_d):
+                if q != cfg.owner:
+                    assert np.array_equal(st["shards"][q], others0[layer][q]), (t, layer, q)
+            # What the next gather of this layer must see.
+            expected[layer] = expected[layer].copy()
+            expected[layer][owner_pos] = rounded
+    # Step 2 really changed the owner's block relative to the initial layer.
+    assert not np.array_equal(expected[0], _stage3_expected_full(O, cfg, p, 0))
