@@ -38,8 +38,11 @@
  *     zero_last_error().  The library never aborts, never prints, and lets no
  *     C++ exception cross the ABI.
  *   - Element offsets and counts are int64.  "16-bit" means ZERO_F16 or
- *     ZERO_BF16.  Buffers must be aligned to their element size; 16-byte
- *     aligned buffers take the vectorised kernels.
+ *     ZERO_BF16.  Buffers must be aligned to their element size.  When every
+ *     base address is 16-byte aligned, the step and the reduction run the
+ *     vector kernel on each piece of the shard whose offsets are multiples
+ *     of 4 elements, after at most 3 leading elements; other pieces run an
+ *     element kernel with the same arithmetic.
  */
 #ifndef ZERO_H_
 #define ZERO_H_
@@ -122,11 +125,14 @@ ZERO_API const char* zero_last_error(void);
  *   out          receives the plan (host memory, immutable, owned by the caller
  *                until zero_plan_destroy).  A plan may be shared by concurrent
  *                calls.
+ * The padded layout must satisfy psi_pad * 4 <= INT64_MAX (fp32 buffers stay
+ * byte-addressable in int64).
  * Rank r owns [flat_off_b + r*S_b, flat_off_b + (r+1)*S_b) of bucket b; its
  * shard is the concatenation of those ranges over buckets (shard_total
  * elements), bucket b's part starting at shard_off_b.
  * Errors: EINVAL for n_d < 1, shard_align < 1, bucket_cap < 0, n_tensors < 0,
- * negative sizes, sizes not summing to psi, or a null pointer; ENOMEM.
+ * negative sizes, sizes not summing to psi, a null pointer, or a padded
+ * layout beyond that bound; ENOMEM.
  */
 ZERO_API zero_status zero_plan(int64_t psi, int32_t n_d, const int64_t* tensor_numel, int32_t n_tensors,
                       int64_t bucket_cap, int32_t shard_align, zero_plan_t* out);
@@ -142,18 +148,29 @@ ZERO_API zero_status zero_plan_bucket(zero_plan_t plan, int32_t b, int64_t* flat
 ZERO_API zero_status zero_plan_tensor(zero_plan_t plan, int32_t t, int32_t* bucket, int64_t* flat_off);
 
 /*
+ * zero_flatten_workspace_bytes -- device workspace zero_flatten needs for this
+ * plan.  Always 0: every copy table travels in the kernel arguments (split
+ * over several launches when a plan has many tensors), so flatten needs no
+ * device memory of its own.  Kept so that callers can size a workspace
+ * without knowing that.
+ */
+ZERO_API size_t zero_flatten_workspace_bytes(zero_plan_t plan);
+
+/*
  * zero_flatten -- pack the ragged tensor list into the padded flat buckets
  * (concept page, design trade-off 1: collectives run over buckets).
- *   tensors  host array of n_tensors device pointers; tensors[t] holds
- *            tensor_numel[t] contiguous elements (may be NULL when that is 0).
- *   dt       element type of tensors and flat (ZERO_F32, ZERO_F16, ZERO_BF16).
- *   flat     device buffer of psi_pad elements.  Tensor t lands at its plan
- *            offset; every padding element is written as zero.
+ *   tensors    host array of n_tensors device pointers; tensors[t] holds
+ *              tensor_numel[t] contiguous elements (may be NULL when that is 0).
+ *   dt         element type of tensors and flat (ZERO_F32, ZERO_F16, ZERO_BF16).
+ *   flat       device buffer of psi_pad elements.  Tensor t lands at its plan
+ *              offset; every padding element is written as zero.
+ *   workspace, ws_bytes  device workspace of zero_flatten_workspace_bytes()
+ *              bytes; may be NULL and 0 (the size is 0).  Not touched.
  * A bit copy.  Errors: EINVAL for nulls, misaligned pointers, or flat
  * overlapping a tensor.
  */
 ZERO_API zero_status zero_flatten(zero_plan_t plan, const void* const* tensors, zero_dtype dt, void* flat,
-                         void* stream);
+                                  void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * zero_shard_reduce -- the arithmetic of reduce-scatter for the owner's
@@ -172,7 +189,7 @@ ZERO_API zero_status zero_flatten(zero_plan_t plan, const void* const* tensors, 
  * overlapping a gradient buffer; EUNSUPPORTED for a non-16-bit dtype.
  */
 ZERO_API zero_status zero_shard_reduce(zero_plan_t plan, int32_t rank, const zero_grad_src* src,
-                              double grad_scale, float* out, void* stream);
+                                       double grad_scale, float* out, void* stream);
 
 /*
  * zero_adam_step -- the owner's mixed-precision Adam update of its shard
@@ -256,22 +273,47 @@ ZERO_API zero_status zero_reshard(zero_plan_t src_plan, zero_plan_t dst_plan, in
  * this library; results are bit-identical whatever it is set to).
  * The fused step reads about ten bytes of gradient for each byte it writes.
  * With a write window, a wave whose results are ready holds its stores until
- * the GPU's constant-rate real-time counter (100 MHz on MI355X: one tick is
- * 10 ns) is within the first open_ticks of a period_ticks-long period, so the
- * device's writes reach HBM in bursts rather than as a thin stream between
- * the reads.
+ * the GPU's constant-rate real-time counter is within the first open_ticks of
+ * a period_ticks-long period, so the device's writes reach HBM in bursts
+ * rather than as a thin stream between the reads.  A tick is one count of
+ * that counter at the rate the device reports as hipDeviceAttributeWallClockRate
+ * (100 MHz on MI355X: 10 ns).
  *   period_ticks  -1: automatic (the default): the library picks the window
- *                 per launch from the rank count and the launch size, and
- *                 uses none for small launches;
+ *                 per launch from the rank count, the launch size, the
+ *                 kernel's occupancy and the counter's rate, and uses none for
+ *                 small launches;
  *                  0: no window, stores issue as soon as results are ready;
  *                 1..100000: this period for every fused or reduce launch.
  *   open_ticks    1..period_ticks when period_ticks > 0; ignored otherwise.
- * The setting is process-wide, applies to launches issued after the call and
- * is safe to change from any thread.  Adam from a `reduced` buffer, the
- * element-wise (unaligned) kernels and the copy kernels never wait.
+ * Scope: this sets the PROCESS-WIDE DEFAULT, read by launches issued after the
+ * call on every stream that has no setting of its own
+ * (zero_set_stream_write_window).  The window assumes the step has HBM to
+ * itself while it runs; a stream whose step overlaps other memory-heavy work
+ * (a collective or a copy on another stream) should turn its own window off
+ * with zero_set_stream_write_window(stream, 0, 0) rather than change the
+ * default for everyone.  Safe to call from any thread.  Adam from a `reduced`
+ * buffer, the element-wise (unaligned) kernels and the copy kernels never
+ * wait.
  * Errors: EINVAL for values outside these ranges (the setting is unchanged).
  */
 ZERO_API zero_status zero_set_write_window(int64_t period_ticks, int64_t open_ticks);
+
+/*
+ * zero_set_stream_write_window -- the same setting for launches on one
+ * stream only; it takes precedence over the process-wide default for every
+ * zero_shard_reduce and fused zero_adam_step call issued on that stream
+ * afterwards, from any thread.
+ *   stream        the hipStream_t the calls are issued on (NULL = the default
+ *                 stream).
+ *   period_ticks  -2: remove the stream's setting (the default applies
+ *                 again); -1: automatic; 0: no window; 1..100000: as above.
+ *   open_ticks    as above.
+ * The library keeps only the stream handle (host memory); remove the setting
+ * before destroying the stream if its handle may be reused.  Safe to call
+ * from any thread.  Errors: EINVAL for values outside these ranges (the
+ * setting is unchanged); ENOMEM.
+ */
+ZERO_API zero_status zero_set_stream_write_window(void* stream, int64_t period_ticks, int64_t open_ticks);
 
 #ifdef __cplusplus
 }

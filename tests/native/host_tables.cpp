@@ -150,6 +150,13 @@ const char* hip_error_string(int) { return "stand-in launch error"; }
 // reduce kernel (arbitrary; the launcher must use whatever it is told), 256 CUs.
 int resident_blocks(int mode, int, int, int, bool) { return mode == kFused ? 1024 : 768; }
 
+// Stand-in real-time counter rate (MI355X reports 100 MHz); tests change it.
+double g_wall_clock_hz = 1e8;
+double wall_clock_hz() { return g_wall_clock_hz; }
+// Stand-in HBM peak (MI355X: 2 GHz x 4 x 8192 bits); tests change it.
+double g_hbm_peak_bps = 8.192e12;
+double hbm_peak_bps() { return g_hbm_peak_bps; }
+
 }  // namespace zk
 
 namespace {
@@ -215,7 +222,13 @@ std::vector<uint8_t> replay_steps(const PlanQ& q, int rank, bool dst_full, uint6
       EXPECT((int64_t)(b_end - g.block_start) * per_block >= g.len, "segment not covered by its blocks");
       EXPECT((int64_t)(b_end - g.block_start - 1) * per_block < g.len, "segment has a block too many");
       EXPECT(g.len >= 1 && g.len <= zk::kSegMaxElems, "segment length %d", g.len);
-      if (r.vec) EXPECT(((g.shard_off | g.full_off | g.dst_off | g.len) & 7) == 0, "vector segment not 8-aligned");
+      if (r.vec) {
+        bool any_full = false;
+        for (int k = 0; k < r.a.n_ranks; ++k) any_full |= ((r.a.full_mask[k >> 5] >> (k & 31)) & 1u) != 0;
+        const bool uses_dst = r.mode != zk::kReduceOnly;
+        EXPECT((g.shard_off & 3) == 0 && (!uses_dst || (g.dst_off & 3) == 0) && (!any_full || (g.full_off & 3) == 0),
+               "vector segment offsets not multiples of 4 elements");
+      }
       int b = -1;
       for (int k = 0; k < q.nb; ++k)
         if (g.shard_off >= q.soff[k] && g.shard_off + g.len <= q.soff[k] + q.sn[k]) b = k;
@@ -313,7 +326,7 @@ void check_reduce(zero_plan_t p, int rank, int64_t shift) {
   int ranks_seen = 0, last_group = -1;
   for (const StepRec& r : g_steps) {
     EXPECT(r.mode == zk::kReduceOnly, "reduce mode");
-    if (shift && q.n_d > 1) EXPECT(!r.vec, "vector kernel chosen for a misaligned gradient");
+    if (shift % 8 && q.n_d > 1) EXPECT(!r.vec, "vector kernel chosen for a gradient not 8-byte aligned");
     const int g0 = (int)(std::find(ptrs.begin(), ptrs.end(), r.a.grad[0]) - ptrs.begin());
     EXPECT(g0 % zk::kMaxRanks == 0, "group starts at rank %d", g0);
     const int grp = g0 / zk::kMaxRanks;
@@ -340,7 +353,7 @@ void check_copies(zero_plan_t p, const std::vector<int64_t>& sizes, Rnd& rnd) {
     tens[t] = sizes[t] ? base + es * rnd.range(0, 8) : nullptr;
   }
   void* flat = make(1, q.psi_pad, es);
-  EXPECT(zero_flatten(p, tens.data(), dt, flat, nullptr) == ZERO_OK, "flatten failed: %s", zero_last_error());
+  EXPECT(zero_flatten(p, tens.data(), dt, flat, nullptr, 0, nullptr) == ZERO_OK, "flatten failed: %s", zero_last_error());
   expect_all_written_once(1, "flat");
   // gather_pack: shards -> full
   g_buf.clear();
@@ -393,7 +406,7 @@ int main() {
     const PlanQ q = query(p);
     const int rank = (int)rnd.range(0, n_d);
     check_step(p, rank, rnd.g() & 1, rnd.g() & 1, (rnd.g() % 4 == 0) ? 4 : 0);
-    check_reduce(p, rank, (rnd.g() % 4 == 0) ? 2 : 0);
+    check_reduce(p, rank, rnd.pick({0, 0, 2, 8}));
     check_copies(p, sizes, rnd);
     if (nt) check_reshard(sizes, psi, rnd);
     zero_plan_destroy(p);
@@ -434,6 +447,8 @@ int main() {
   // Write-window setting: range checks, forced values reach every fused and
   // reduce launch, and -1 restores the automatic choice.
   EXPECT(zero_set_write_window(-2, 0) == ZERO_EINVAL, "period -2 accepted");
+  EXPECT(zero_set_stream_write_window(nullptr, -3, 0) == ZERO_EINVAL, "stream period -3 accepted");
+  EXPECT(zero_set_stream_write_window(nullptr, 100, 101) == ZERO_EINVAL, "stream open > period accepted");
   EXPECT(zero_set_write_window(100001, 1) == ZERO_EINVAL, "period above 1 ms accepted");
   EXPECT(zero_set_write_window(100, 0) == ZERO_EINVAL, "open 0 accepted");
   EXPECT(zero_set_write_window(100, 101) == ZERO_EINVAL, "open > period accepted");
@@ -511,6 +526,123 @@ int main() {
     EXPECT(g_steps.size() == 1 && g_steps[0].a.win_period == 0, "automatic window with 8 ranks");
     zero_plan_destroy(p8);
     (void)q;
+    zero_plan_destroy(p);
+  }
+  // Scope of the setting: a stream's own setting wins on that stream only;
+  // -2 returns the stream to the process-wide default.
+  {
+    std::vector<int64_t> sizes = {((int64_t)1 << 25) * 64};
+    zero_plan_t p;
+    zero_plan(sizes[0], 64, sizes.data(), 1, 0, 64, &p);
+    std::vector<const void*> ptrs(64);
+    for (int r = 0; r < 64; ++r) ptrs[r] = (const void*)(uintptr_t)fake_base(100 + r);
+    zero_grad_src src = {ZERO_BF16, 64, ptrs.data(), nullptr};
+    zero_adam_hyper hp = {1e-4, 0.9, 0.999, 1e-8, 1.0 / 64};
+    void* sa = (void*)(uintptr_t)0x1000;
+    void* sb = (void*)(uintptr_t)0x2000;
+    auto window_on = [&](void* stream) {
+      g_steps.clear();
+      EXPECT(zero_adam_step(p, 0, &hp, 1, &src, nullptr, (float*)(uintptr_t)fake_base(1),
+                            (float*)(uintptr_t)fake_base(2), (float*)(uintptr_t)fake_base(3),
+                            (void*)(uintptr_t)fake_base(4), ZERO_F16, 1, stream) == ZERO_OK,
+             "scoped step failed: %s", zero_last_error());
+      return g_steps.empty() ? std::pair<uint32_t, uint32_t>{~0u, ~0u}
+                             : std::pair<uint32_t, uint32_t>{g_steps[0].a.win_period, g_steps[0].a.win_open};
+    };
+    const auto automatic = window_on(sa);
+    EXPECT(automatic.first > 0, "no automatic window on a large launch");
+    EXPECT(zero_set_stream_write_window(sa, 0, 0) == ZERO_OK, "stream setting refused");
+    EXPECT(zero_set_stream_write_window(nullptr, 3000, 300) == ZERO_OK, "null-stream setting refused");
+    EXPECT(window_on(sa) == std::make_pair(0u, 0u), "stream A: own setting (off) not used");
+    EXPECT(window_on(sb) == automatic, "stream B: changed by stream A's setting");
+    EXPECT(window_on(nullptr) == std::make_pair(3000u, 300u), "default stream: own setting not used");
+    EXPECT(zero_set_write_window(0, 0) == ZERO_OK, "default setting refused");
+    EXPECT(window_on(sb) == std::make_pair(0u, 0u), "stream B: process default not followed");
+    EXPECT(zero_set_stream_write_window(sa, 5000, 500) == ZERO_OK, "stream update refused");
+    EXPECT(window_on(sa) == std::make_pair(5000u, 500u), "stream A: updated setting not used");
+    EXPECT(zero_set_stream_write_window(sa, -2, 0) == ZERO_OK, "stream reset refused");
+    EXPECT(zero_set_stream_write_window(nullptr, -2, 0) == ZERO_OK, "null-stream reset refused");
+    EXPECT(window_on(sa) == std::make_pair(0u, 0u), "stream A: not back on the default");
+    EXPECT(zero_set_write_window(-1, 0) == ZERO_OK, "automatic default refused");
+    EXPECT(window_on(sa) == automatic && window_on(nullptr) == automatic, "not back to automatic");
+    // The automatic period follows the counter rate the device reports: the
+    // same launch at 50, 100 and 200 MHz takes 2484, 4968 and 9937 ticks
+    // (1024 resident x 4096 elements x 154 B at 6.5 TB/s, halved); no rate,
+    // no window.
+    const double rates[3] = {5e7, 1e8, 2e8};
+    const uint32_t want_p[3] = {2484, 4968, 9937}, want_o[3] = {225, 451, 903};
+    for (int i = 0; i < 3; ++i) {
+      zk::g_wall_clock_hz = rates[i];
+      EXPECT(window_on(sb) == std::make_pair(want_p[i], want_o[i]), "automatic window at %.0f Hz: (%u, %u)",
+             rates[i], window_on(sb).first, window_on(sb).second);
+    }
+    zk::g_wall_clock_hz = 0;
+    EXPECT(window_on(sb) == std::make_pair(0u, 0u), "automatic window without a counter rate");
+    zk::g_wall_clock_hz = 1e8;
+    zero_plan_destroy(p);
+  }
+  // The plain Psi / N_d layout (align 1) of the 7.5B workload: every owner's
+  // shard of 117,187,500 elements starts at a multiple of 4, so each runs
+  // entirely in the vector kernel (tables only, no memory behind them).
+  {
+    std::vector<int64_t> sizes = {7500000000LL};
+    zero_plan_t p;
+    zero_plan(sizes[0], 64, sizes.data(), 1, 0, 1, &p);
+    int64_t S = 0;
+    zero_plan_info(p, nullptr, &S, nullptr, nullptr);
+    EXPECT(S == 117187500, "align-1 shard %lld", (long long)S);
+    // The 64 slices as rows of one [64, S] bf16 tensor: every other row starts
+    // 8 bytes past a 16-byte boundary, which the vector kernel accepts.
+    std::vector<const void*> ptrs(64);
+    for (int r = 0; r < 64; ++r) ptrs[r] = (const void*)(uintptr_t)(fake_base(100) + (uint64_t)r * S * 2);
+    EXPECT(((uintptr_t)ptrs[1] & 15) == 8, "row 1 of the slice tensor should be 8 bytes off");
+    zero_grad_src src = {ZERO_BF16, 64, ptrs.data(), nullptr};
+    zero_adam_hyper hp = {1e-4, 0.9, 0.999, 1e-8, 1.0 / 64};
+    for (int owner : {0, 1, 63}) {
+      g_steps.clear();
+      EXPECT(zero_adam_step(p, owner, &hp, 1, &src, nullptr, (float*)(uintptr_t)fake_base(1),
+                            (float*)(uintptr_t)fake_base(2), (float*)(uintptr_t)fake_base(3),
+                            (void*)(uintptr_t)fake_base(4), ZERO_F16, 1, nullptr) == ZERO_OK,
+             "align-1 step failed: %s", zero_last_error());
+      int64_t vec_elems = 0;
+      bool all_vec = true;
+      for (const auto& r : g_steps) {
+        all_vec &= r.vec;
+        for (int k = 0; k < r.a.n_seg; ++k) vec_elems += r.vec ? r.a.seg[k].len : 0;
+      }
+      EXPECT(all_vec && vec_elems == S, "align-1 owner %d: %lld of %lld elements in the vector kernel", owner,
+             (long long)vec_elems, (long long)S);
+    }
+    // The same with the reduction, whose output is fp32 and 16-byte aligned.
+    g_steps.clear();
+    EXPECT(zero_shard_reduce(p, 5, &src, 1.0 / 64, (float*)(uintptr_t)fake_base(5), nullptr) == ZERO_OK,
+           "align-1 reduce failed: %s", zero_last_error());
+    EXPECT(g_steps.size() == 1 && g_steps[0].vec, "align-1 reduce not in the vector kernel");
+    // A 16-bit destination only 8-byte aligned is fine too; an fp32 state
+    // array 8 bytes off is not.
+    g_steps.clear();
+    EXPECT(zero_adam_step(p, 0, &hp, 1, &src, nullptr, (float*)(uintptr_t)fake_base(1),
+                          (float*)(uintptr_t)fake_base(2), (float*)(uintptr_t)fake_base(3),
+                          (void*)(uintptr_t)(fake_base(4) + 8), ZERO_F16, 1, nullptr) == ZERO_OK,
+           "8-byte destination: %s", zero_last_error());
+    EXPECT(!g_steps.empty() && g_steps[0].vec, "8-byte aligned destination refused by the vector kernel");
+    g_steps.clear();
+    EXPECT(zero_adam_step(p, 0, &hp, 1, &src, nullptr, (float*)(uintptr_t)(fake_base(1) + 8),
+                          (float*)(uintptr_t)fake_base(2), (float*)(uintptr_t)fake_base(3),
+                          (void*)(uintptr_t)fake_base(4), ZERO_F16, 1, nullptr) == ZERO_OK,
+           "8-byte master: %s", zero_last_error());
+    EXPECT(!g_steps.empty() && !g_steps[0].vec, "fp32 state 8 bytes off given to the vector kernel");
+    zero_plan_destroy(p);
+  }
+  // A plan whose padded layout would overflow int64 byte offsets is refused.
+  {
+    std::vector<int64_t> sizes = {1, 1, 1, 1, 1};
+    zero_plan_t p = nullptr;
+    EXPECT(zero_plan(5, 1 << 30, sizes.data(), 5, 1, 1 << 30, &p) == ZERO_EINVAL && p == nullptr,
+           "overflowing padded layout accepted");
+    EXPECT(strstr(zero_last_error(), "padded layout") != nullptr, "overflow error text: %s", zero_last_error());
+    EXPECT(zero_plan(5, 1 << 20, sizes.data(), 5, 1, 1 << 10, &p) == ZERO_OK && p != nullptr,
+           "large but valid padded layout refused: %s", zero_last_error());
     zero_plan_destroy(p);
   }
   // More buckets than one launch's segment table.

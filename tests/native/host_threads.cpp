@@ -36,6 +36,8 @@ int launch_copy(const CopyArgs& a, int, int n_blocks, void*) {
 }
 const char* hip_error_string(int) { return "stand-in"; }
 int resident_blocks(int, int, int, int, bool) { return 1024; }
+double wall_clock_hz() { return 1e8; }
+double hbm_peak_bps() { return 8.192e12; }
 }  // namespace zk
 
 namespace {
@@ -66,9 +68,10 @@ void worker(int tid, zero_plan_t shared) {
       zero_grad_src src = {ZERO_BF16, nd, ptrs.data(), nullptr};
       zero_adam_hyper hp = {1e-4, 0.9, 0.999, 1e-8, 1.0 / nd};
       expect(zero_adam_step(p, it % nd, &hp, it + 1, &src, nullptr, (float*)addr(1), (float*)addr(2),
-                            (float*)addr(3), addr(4), ZERO_F16, 1, nullptr) == ZERO_OK,
+                            (float*)addr(3), addr(4), ZERO_F16, 1, (void*)(uintptr_t)(0x100 * (1 + tid % 4))) == ZERO_OK,
              "step");
-      expect(zero_shard_reduce(p, 0, &src, 0.25, (float*)addr(5), nullptr) == ZERO_OK, "reduce");
+      expect(zero_shard_reduce(p, 0, &src, 0.25, (float*)addr(5), (void*)(uintptr_t)(0x100 * (1 + it % 4))) == ZERO_OK,
+             "reduce");
       std::vector<const void*> shards(nd);
       for (int q = 0; q < nd; ++q) shards[q] = addr(200 + q);
       expect(zero_gather_pack(p, shards.data(), ZERO_BF16, addr(6), nullptr) == ZERO_OK, "gather");
@@ -77,7 +80,7 @@ void worker(int tid, zero_plan_t shared) {
       expect(zero_plan_tensor(p, 0, &b, &off) == ZERO_OK, "tensor");
     }
     const void* tens[4] = {addr(300), addr(301), addr(302), addr(303)};
-    expect(zero_flatten(own, tens, ZERO_F32, addr(7), nullptr) == ZERO_OK, "flatten");
+    expect(zero_flatten(own, tens, ZERO_F32, addr(7), nullptr, 0, nullptr) == ZERO_OK, "flatten");
     // A planted bad call: this thread's error text names its own mistake.
     const std::string want = "rank " + std::to_string(-1 - tid);
     expect(zero_shard_reduce(own, -1 - tid, nullptr, 1.0, nullptr, nullptr) == ZERO_EINVAL, "bad rank");
@@ -98,6 +101,10 @@ int main() {
       if (i % 3 == 0) zero_set_write_window(-1, 0);
       else if (i % 3 == 1) zero_set_write_window(0, 0);
       else zero_set_write_window(1000 + i % 500, 100);
+      // Per-stream settings on the streams the workers launch on.
+      void* s = (void*)(uintptr_t)(0x100 * (1 + i % 4));
+      if (i % 5 == 0) zero_set_stream_write_window(s, -2, 0);
+      else zero_set_stream_write_window(s, i % 2 ? 0 : 2000, 200);
     }
   });
   std::vector<std::thread> ts;

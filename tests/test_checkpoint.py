@@ -28,6 +28,54 @@ def test_save_load_round_trip(tmp_path):
         C.save_shard(str(tmp_path / "bad.npz"), args, 0, 1, x[0].astype(np.float64), x[1], x[2])
 
 
+def _write_raw(path, meta, arrays):
+    """A checkpoint file written without save_shard's checks (a damaged or
+    foreign file)."""
+    import json
+    np.savez(path, meta=np.frombuffer(json.dumps(meta).encode(), dtype=np.uint8), **arrays)
+
+
+def test_bad_checkpoints_rejected_before_any_gpu_call(tmp_path, monkeypatch):
+    """save_shard refuses arrays that do not match the plan; load_shard and
+    restore refuse truncated, float64 or two-dimensional arrays, before
+    anything is copied to a device or reaches libzero."""
+    import zero_sharded_mixed_02_amd as Z
+    from zero_sharded_mixed_02_amd import checkpoint as C
+    args = {"psi": 3000, "n_d": 3, "tensor_numel": [1000, 2000], "bucket_cap": 0, "shard_align": 8}
+    S = C.plan_from(args).shard_total
+    good = [np.zeros(S, np.float32) for _ in range(3)]
+    with pytest.raises(ValueError, match="holds"):
+        C.save_shard(str(tmp_path / "a.npz"), args, 0, 1, good[0][:-1], good[1], good[2])
+    with pytest.raises(ValueError, match="float32"):
+        C.save_shard(str(tmp_path / "a.npz"), args, 0, 1, good[0], good[1].astype(np.float64), good[2])
+    with pytest.raises(ValueError, match="rank"):
+        C.save_shard(str(tmp_path / "a.npz"), args, 3, 1, *good)
+    assert not (tmp_path / "a.npz").exists()
+    meta = {"format": C.FORMAT, "t": 4, "plan": args}
+    damaged = {
+        "truncated": {"master": good[0][:-8], "m": good[1], "v": good[2]},
+        "float64": {"master": good[0], "m": good[1].astype(np.float64), "v": good[2]},
+        "2-d": {"master": good[0], "m": good[1], "v": good[2].reshape(1, S)},
+    }
+    # Nothing below may reach the GPU library or torch's device copies.
+    monkeypatch.setattr(Z, "zero_reshard", lambda *a, **k: (_ for _ in ()).throw(AssertionError("reshard called")))
+    monkeypatch.setattr(C, "zero_reshard", lambda *a, **k: (_ for _ in ()).throw(AssertionError("reshard called")))
+    new_plan = C.plan_from(dict(args, n_d=2))
+    for name, arrays in damaged.items():
+        paths = []
+        for r in range(3):
+            p = str(tmp_path / f"{name}{r}.npz")
+            if r == 1:
+                _write_raw(p, dict(meta, rank=r), arrays)
+            else:
+                C.save_shard(p, args, r, 4, *good)
+            paths.append(p)
+        with pytest.raises(ValueError):
+            C.load_shard(paths[1])
+        with pytest.raises(ValueError):
+            C.restore(paths, new_plan, 0, device="cpu")
+
+
 @pytest.mark.gpu
 def test_restore_at_other_degree(gpu, oracle_lib, tmp_path):
     import zero_sharded_mixed_02_amd as Z

@@ -33,11 +33,20 @@ def _free(run):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name", ["7.5B-stage2", "13B-stage1"])
+def _full_size_config(name):
+    from dataclasses import replace
+    from synth.workloads import with_owner
+    if name == "7.5B-stage2-align1-owner17":
+        # The plain Psi/N_d layout: S = 117,187,500, offsets multiples of 4.
+        return with_owner(replace(WORKLOADS["7.5B-stage2"], align=1, steps=2), 17)
+    return WORKLOADS[name]
+
+
+@pytest.mark.parametrize("name", ["7.5B-stage2", "13B-stage1", "7.5B-stage2-align1-owner17"])
 def test_stage12_full_size(gpu, oracle_lib, name):
     import torch
     from oracle.runner import OracleRun
-    cfg = WORKLOADS[name]
+    cfg = _full_size_config(name)
     say(f"[full size] {cfg.name}: psi={cfg.psi} n_d={cfg.n_d} steps={cfg.steps}")
     run = GpuRun(cfg)
     say(f"  resident {run.bytes_resident() / 1e9:.1f} GB, S={run.S}")

@@ -42,6 +42,17 @@ SMALL_CASES = {
     "manybuckets-nd4-align8": Config("manybuckets", tuple([37] * 150), n_d=4, gdt=F16, pdt=F16,
                                      owner=3, bucket_cap=37, align=8, steps=2, seed=14),
     "smaller-than-nd-align": small_config(10, 4, BF16, F16, owner=2, steps=2, seed=15),
+    # Align 1: shard lengths and offsets not multiples of 4.  Owner 0 of the
+    # tiny workload runs the vector kernel with a 1-element tail; the buckets
+    # below mix pieces with leading elements, tails, and pieces whose offsets
+    # disagree modulo 4 (element kernel).
+    "align1-owner0-tail": replace(WORKLOADS["tiny"], align=1, owner=0),
+    "align1-multibucket-heads": Config("a1mb", (1001, 2002, 3003, 4004, 5005, 6006, 7, 30_001), n_d=3,
+                                       gdt=BF16, pdt=F16, owner=1, bucket_cap=5000, align=1, steps=2, seed=18),
+    "align1-stage1-full": small_config(100_010, 2, F16, BF16, owner=1, steps=2, seed=19, stage=1, align=1,
+                                       full_ranks=(0, 1)),
+    "align2-nd5-heads": Config("a2", (999, 12_347, 5, 70_001), n_d=5, gdt=F16, pdt=F16, owner=3,
+                               bucket_cap=13_000, align=2, steps=2, seed=20),
 }
 
 
@@ -93,7 +104,8 @@ def test_gpt2_small_every_owner_one_step(gpu, oracle_lib):
 
 
 @pytest.mark.parametrize("name", ["tiny-owner3-pad", "nd3-generic", "stage1-nd5-somefull",
-                                  "manybuckets-nd4-align8", "tiny-align1-elem"])
+                                  "manybuckets-nd4-align8", "tiny-align1-elem", "align1-owner0-tail",
+                                  "align1-multibucket-heads", "align2-nd5-heads"])
 def test_fused_equals_unfused(gpu, oracle_lib, name):
     """zero_shard_reduce then zero_adam_step(reduced) gives exactly the fused
     step; the reduced gradient itself matches the oracle's fold."""
@@ -198,6 +210,30 @@ def test_write_windows_change_nothing(gpu, oracle_lib, zero_lib, window):
         want = O.reduce(ref.layers[0]["slices"], cfg.gdt, float(np.float32(cfg.grad_scale)))
         assert_f32(red.cpu().numpy(), want, "reduced", bitwise=True)
     finally:
+        Z.zero_set_write_window(-1)
+
+
+def test_stream_write_window_changes_nothing(gpu, oracle_lib, zero_lib):
+    """A window set for one stream only (zero_set_stream_write_window) applies
+    to launches on that stream and leaves every result bit unchanged; the
+    stream's setting removed, the process default applies again."""
+    import torch
+    Z = zero_lib
+    cfg = SMALL_CASES["nd64-lastrank"]
+    stream = torch.cuda.current_stream().cuda_stream
+    say("[stream window] forced 3 us / 10 ns on the current stream, default off")
+    Z.zero_set_write_window(0, 0)
+    Z.zero_set_stream_write_window(stream, 300, 1)
+    try:
+        run, ref = run_pair(cfg)
+        assert_state(run.fetch(), ref.state(), cfg.pdt, "stream window")
+        side = torch.cuda.Stream()
+        with torch.cuda.stream(side):
+            run2, ref2 = run_pair(replace(cfg, seed=cfg.seed + 1))
+        torch.cuda.synchronize()
+        assert_state(run2.fetch(), ref2.state(), cfg.pdt, "other stream")
+    finally:
+        Z.zero_set_stream_write_window(stream, -2)
         Z.zero_set_write_window(-1)
 
 

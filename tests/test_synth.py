@@ -14,7 +14,7 @@ def _positions(n, seed):
 
 @pytest.mark.parametrize("mix", [False, True])
 def test_c_matches_numpy(mix):
-    pos = _positions(500_000, 1)
+    pos = _positions(2_000_000, 1)
     k, ks = synth.key_of(3, synth.STREAM_GRAD, 17, 6), synth.key_of(3, synth.STREAM_MIXSEL, 17, 6)
     a = synth.mix_f32(k, ks, pos, 1e-3) if mix else synth.normal_f32(k, pos, 1e-3)
     b = synth.mix_f32_np(k, ks, pos, 1e-3) if mix else synth.normal_f32_np(k, pos, 1e-3)
@@ -22,14 +22,40 @@ def test_c_matches_numpy(mix):
 
 
 def test_draw_statistics():
-    pos = np.arange(2_000_000, dtype=np.int64)
+    """The draws are N(0, sigma) as the workloads state (Box-Muller, tails to
+    5.77 sigma): mean, spread, two- and three-sigma tail shares, kurtosis and
+    the bound; and the zero/outlier mix rates of the 13B workload."""
+    pos = np.arange(4_000_000, dtype=np.int64)
     x = synth.normal_f32(synth.key_of(1, synth.STREAM_GRAD, 0, 1), pos, 1e-3).astype(np.float64)
-    assert abs(x.mean()) < 5e-6 and abs(x.std() - 1e-3) < 1e-5
-    assert np.abs(x).max() <= 1e-3 * 3.47
+    assert abs(x.mean()) < 3e-6 and abs(x.std() - 1e-3) < 3e-6
+    assert abs((np.abs(x) > 2e-3).mean() - 0.045500) < 5e-4        # 2 P(Z > 2)
+    assert abs((np.abs(x) > 3e-3).mean() - 0.002700) < 1.5e-4      # 2 P(Z > 3)
+    kurt = ((x - x.mean()) ** 4).mean() / x.var() ** 2
+    assert abs(kurt - 3.0) < 0.02
+    assert np.abs(x).max() <= 1e-3 * synth.Z_MAX * (1 + 1e-6)
     y = synth.mix_f32(synth.key_of(4, synth.STREAM_GRAD, 0, 1), synth.key_of(4, synth.STREAM_MIXSEL, 0, 1),
                       pos, 1e-3)
     assert abs((y == 0).mean() - 0.01) < 5e-4
     assert abs((np.abs(y) == 100).mean() - 0.001) < 1.5e-4
+
+
+def test_unit_normal_follows_box_muller():
+    """The fp32 sequence computes sqrt(-2 ln u1) cos(2 pi u2) of the hash's two
+    24-bit uniforms to within 4e-7 of the radius (float64 reference with
+    numpy's log and cos), including the extreme hashes."""
+    rng = np.random.default_rng(0)
+    u = rng.integers(0, 2 ** 32, size=2_000_000, dtype=np.uint64) << np.uint64(32)
+    u |= rng.integers(0, 2 ** 32, size=2_000_000, dtype=np.uint64)
+    edge = np.array([0, (2 ** 24 - 1) << 40, 0xFFFFFFFFFFFFFFFF, 0x3FFFFF00, 0x400000 << 8, 0xFFFFFF00],
+                    dtype=np.uint64)
+    u = np.concatenate([u, edge])
+    z32 = synth.unit_normal_np(u).astype(np.float64)
+    u1 = ((u >> np.uint64(40)) + np.uint64(1)).astype(np.float64) / 2 ** 24
+    u2 = ((u & np.uint64(0xFFFFFFFF)) >> np.uint64(8)).astype(np.float64) / 2 ** 24
+    r = np.sqrt(-2.0 * np.log(u1))
+    z = r * np.cos(2.0 * np.pi * u2)
+    assert np.all(np.abs(z32 - z) <= 4e-7 * r + 1e-30)
+    assert z32[-6] == np.float32(synth.Z_MAX) or abs(z32[-6] - synth.Z_MAX) < 4e-6   # u1 = 2^-24, angle 0
 
 
 def test_streams_are_distinct():

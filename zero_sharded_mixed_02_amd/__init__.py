@@ -7,9 +7,14 @@ addresses and streams to ``hipStream_t`` handles, and raises ``ZeroError`` on a
 non-OK status.  All computation happens in the HIP kernels of libzero.so; if
 the library has not been built, loading fails loudly (there is no fallback).
 
-Tensors may be passed as ``torch.Tensor`` (their ``data_ptr()`` is used) or as
-plain integer device addresses.  ``stream=None`` means torch's current stream
-on the current device.
+Tensors may be passed as ``torch.Tensor`` or as plain integer device
+addresses.  A tensor is checked against the plan before the C call -- a
+contiguous GPU tensor of the right element size holding at least the elements
+the plan needs (exactly tensor t's size for flatten inputs) -- and pointer
+lists must have one entry per rank or tensor; a failed check raises
+``ValueError`` and nothing is launched.  A plain integer address is passed
+through unchecked: the caller vouches for it.  ``stream=None`` means torch's
+current stream on the current device.
 """
 from __future__ import annotations
 
@@ -29,9 +34,9 @@ STATUS_NAMES = {0: "ZERO_OK", -1: "ZERO_EINVAL", -2: "ZERO_EUNSUPPORTED", -3: "Z
 
 # Names of every entry point include/zero.h declares.
 ENTRY_POINTS = ("zero_version", "zero_last_error", "zero_plan", "zero_plan_destroy",
-                "zero_plan_info", "zero_plan_bucket", "zero_plan_tensor", "zero_flatten",
-                "zero_shard_reduce", "zero_adam_step", "zero_gather_pack", "zero_reshard",
-                "zero_set_write_window")
+                "zero_plan_info", "zero_plan_bucket", "zero_plan_tensor", "zero_flatten_workspace_bytes",
+                "zero_flatten", "zero_shard_reduce", "zero_adam_step", "zero_gather_pack", "zero_reshard",
+                "zero_set_write_window", "zero_set_stream_write_window")
 
 
 class ZeroError(RuntimeError):
@@ -90,8 +95,10 @@ def load():
     L.zero_plan_bucket.argtypes = [vp, i32, p_i64, p_i64, p_i64, p_i64, p_i64]
     L.zero_plan_tensor.restype = i32
     L.zero_plan_tensor.argtypes = [vp, i32, p_i32, p_i64]
+    L.zero_flatten_workspace_bytes.restype = ctypes.c_size_t
+    L.zero_flatten_workspace_bytes.argtypes = [vp]
     L.zero_flatten.restype = i32
-    L.zero_flatten.argtypes = [vp, ctypes.POINTER(vp), i32, vp, vp]
+    L.zero_flatten.argtypes = [vp, ctypes.POINTER(vp), i32, vp, vp, ctypes.c_size_t, vp]
     L.zero_shard_reduce.restype = i32
     L.zero_shard_reduce.argtypes = [vp, i32, ctypes.POINTER(_GradSrc), ctypes.c_double, vp, vp]
     L.zero_adam_step.restype = i32
@@ -103,6 +110,8 @@ def load():
     L.zero_reshard.argtypes = [vp, vp, i32, ctypes.POINTER(vp), i32, vp, vp]
     L.zero_set_write_window.restype = i32
     L.zero_set_write_window.argtypes = [i64, i64]
+    L.zero_set_stream_write_window.restype = i32
+    L.zero_set_stream_write_window.argtypes = [vp, i64, i64]
     _lib = L
     return L
 
@@ -120,6 +129,53 @@ def _addr(x) -> int:
     return int(x.data_ptr())
 
 
+ESIZE = {ZERO_F32: 4, ZERO_F16: 2, ZERO_BF16: 2}
+
+
+def _esize(dt: int) -> int:
+    if dt not in ESIZE:
+        raise ValueError(f"unknown dtype {dt}")
+    return ESIZE[dt]
+
+
+def _tensor_props(x, name: str, esize: int):
+    """(element count, on a GPU) of tensor x after checking what does not
+    depend on the plan: a contiguous tensor whose elements are esize bytes."""
+    if not hasattr(x, "data_ptr") or not hasattr(x, "element_size"):
+        raise TypeError(f"{name}: expected a torch tensor or an integer device address, got {type(x).__name__}")
+    if x.element_size() != esize:
+        raise ValueError(f"{name}: elements of {x.element_size()} bytes ({x.dtype}), expected {esize}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} is not contiguous")
+    return int(x.numel()), x.device.type == "cuda"
+
+
+def _arg(x, name: str, esize: int, need: int, exact: bool = False) -> int:
+    """Device address of x.  A tensor must be a contiguous GPU tensor holding
+    at least `need` elements of esize bytes (exactly `need` with exact=True);
+    None and integer addresses are passed through (the C side rejects a NULL
+    it cannot accept)."""
+    if x is None or isinstance(x, int):
+        return _addr(x)
+    n, on_gpu = _tensor_props(x, name, esize)
+    if n < need or (exact and n != need):
+        raise ValueError(f"{name} holds {n} elements, the plan needs {'exactly ' if exact else ''}{need}")
+    if not on_gpu:
+        raise ValueError(f"{name} is not on a GPU ({x.device})")
+    return int(x.data_ptr())
+
+
+def _arg_list(xs, name: str, count: int, esize: int, need: int, exact: bool = False) -> ctypes.Array:
+    if xs is None:
+        raise ValueError(f"{name} is None")
+    xs = list(xs)
+    if len(xs) != count:
+        raise ValueError(f"{name} has {len(xs)} entries, the plan needs {count}")
+    addrs = [_arg(x, f"{name}[{i}]", esize, need[i] if isinstance(need, (list, tuple)) else need, exact)
+             for i, x in enumerate(xs)]
+    return (ctypes.c_void_p * max(1, count))(*addrs)
+
+
 def _stream(stream) -> int:
     if stream is None:
         import torch
@@ -127,10 +183,6 @@ def _stream(stream) -> int:
     if isinstance(stream, int):
         return stream
     return int(stream.cuda_stream)
-
-
-def _ptr_array(xs) -> ctypes.Array:
-    return (ctypes.c_void_p * max(1, len(xs)))(*[_addr(x) for x in xs])
 
 
 def zero_version() -> int:
@@ -141,10 +193,20 @@ WINDOW_AUTO = -1
 
 
 def zero_set_write_window(period_ticks: int, open_ticks: int = 0) -> None:
-    """Store scheduling of the fused step and the reduction (results are
-    identical): -1 automatic (default), 0 none, else a period of period_ticks
-    real-time-counter ticks (10 ns) whose first open_ticks admit stores."""
+    """Process-wide default store scheduling of the fused step and the
+    reduction (results are identical): -1 automatic (default), 0 none, else a
+    period of period_ticks real-time-counter ticks whose first open_ticks
+    admit stores."""
     _check(load().zero_set_write_window(period_ticks, open_ticks))
+
+
+WINDOW_INHERIT = -2
+
+
+def zero_set_stream_write_window(stream, period_ticks: int, open_ticks: int = 0) -> None:
+    """The same setting for launches on one stream only; -2 removes the
+    stream's own setting so it follows the process-wide default again."""
+    _check(load().zero_set_stream_write_window(_stream(stream), period_ticks, open_ticks))
 
 
 def zero_last_error() -> str:
@@ -154,9 +216,10 @@ def zero_last_error() -> str:
 class Plan:
     """Owner of a zero_plan_t handle, with its queries."""
 
-    def __init__(self, handle: int, n_tensors: int):
+    def __init__(self, handle: int, tensor_numel: Sequence[int]):
         self._h = ctypes.c_void_p(handle)
-        self.n_tensors = n_tensors
+        self.tensor_numel = [int(n) for n in tensor_numel]
+        self.n_tensors = len(self.tensor_numel)
         L = load()
         psi_pad, shard_total = ctypes.c_int64(), ctypes.c_int64()
         nb, nd = ctypes.c_int32(), ctypes.c_int32()
@@ -202,45 +265,103 @@ def zero_plan(psi: int, n_d: int, tensor_numel: Sequence[int], bucket_cap: int =
     arr = (ctypes.c_int64 * max(1, n))(*tensor_numel)
     h = ctypes.c_void_p()
     _check(load().zero_plan(psi, n_d, arr, n, bucket_cap, shard_align, ctypes.byref(h)))
-    return Plan(h.value, n)
+    return Plan(h.value, tensor_numel)
 
 
 class GradSrc:
-    """The N_d gradient contributions (zero_grad_src)."""
+    """The N_d gradient contributions (zero_grad_src).  Tensors are checked
+    here (16-bit elements, contiguous, on a GPU) and kept referenced; their
+    sizes are compared with the plan at every call."""
 
     def __init__(self, dtype: int, ptrs: Sequence, is_full: Optional[Sequence[int]] = None):
+        if dtype not in (ZERO_F16, ZERO_BF16):
+            raise ValueError(f"gradient dtype {dtype} is not 16-bit")
+        ptrs = list(ptrs)
         self.dtype = dtype
-        self._ptrs = _ptr_array(ptrs)
         self.n = len(ptrs)
-        self._full = None if is_full is None else (ctypes.c_uint8 * max(1, len(is_full)))(*is_full)
+        if is_full is not None and len(is_full) != self.n:
+            raise ValueError(f"is_full has {len(is_full)} entries for {self.n} gradient buffers")
+        self.is_full = [0] * self.n if is_full is None else [1 if f else 0 for f in is_full]
+        self._keep = ptrs
+        # Smallest tensor among the compact and among the full contributions
+        # (plain addresses are not counted: the caller vouches for them).
+        self.min_compact = self.min_full = None
+        self.not_on_gpu = None   # name of the first tensor that is not on a GPU
+        for q, x in enumerate(ptrs):
+            if x is None or isinstance(x, int):
+                continue
+            n, on_gpu = _tensor_props(x, f"gradient of rank {q}", 2)
+            if not on_gpu and self.not_on_gpu is None:
+                self.not_on_gpu = f"gradient of rank {q} ({x.device})"
+            if self.is_full[q]:
+                self.min_full = n if self.min_full is None else min(self.min_full, n)
+            else:
+                self.min_compact = n if self.min_compact is None else min(self.min_compact, n)
+        self._ptrs = (ctypes.c_void_p * max(1, self.n))(*[_addr(x) for x in ptrs])
+        self._full = None if is_full is None else (ctypes.c_uint8 * max(1, self.n))(*self.is_full)
         self.c = _GradSrc(dtype, self.n, ctypes.cast(self._ptrs, ctypes.POINTER(ctypes.c_void_p)),
                           None if self._full is None else ctypes.cast(self._full, ctypes.POINTER(ctypes.c_uint8)))
 
+    def check(self, plan: "Plan") -> None:
+        if self.n != plan.n_d:
+            raise ValueError(f"gradient source has {self.n} ranks, the plan has n_d={plan.n_d}")
+        if self.min_compact is not None and self.min_compact < plan.shard_total:
+            raise ValueError(f"a compact gradient slice holds {self.min_compact} elements, "
+                             f"the plan needs {plan.shard_total}")
+        if self.min_full is not None and self.min_full < plan.psi_pad:
+            raise ValueError(f"a full gradient buffer holds {self.min_full} elements, the plan needs {plan.psi_pad}")
+        if self.not_on_gpu is not None:
+            raise ValueError(f"{self.not_on_gpu} is not on a GPU")
 
-def zero_flatten(plan: Plan, tensors: Sequence, dt: int, flat, stream=None) -> None:
-    _check(load().zero_flatten(plan.handle, _ptr_array(tensors), dt, _addr(flat), _stream(stream)))
+
+def zero_flatten_workspace_bytes(plan: Plan) -> int:
+    return int(load().zero_flatten_workspace_bytes(plan.handle))
+
+
+def zero_flatten(plan: Plan, tensors: Sequence, dt: int, flat, stream=None, workspace=None,
+                 ws_bytes: int = 0) -> None:
+    es = _esize(dt)
+    arr = _arg_list(tensors, "tensors", plan.n_tensors, es, plan.tensor_numel, exact=True)
+    out = _arg(flat, "flat", es, plan.psi_pad)
+    ws = _addr(workspace)
+    _check(load().zero_flatten(plan.handle, arr, dt, out, ws, ws_bytes, _stream(stream)))
 
 
 def zero_shard_reduce(plan: Plan, rank: int, src: GradSrc, grad_scale: float, out, stream=None) -> None:
-    _check(load().zero_shard_reduce(plan.handle, rank, ctypes.byref(src.c), grad_scale, _addr(out),
-                                    _stream(stream)))
+    src.check(plan)
+    o = _arg(out, "out", 4, plan.shard_total)
+    _check(load().zero_shard_reduce(plan.handle, rank, ctypes.byref(src.c), grad_scale, o, _stream(stream)))
 
 
 def zero_adam_step(plan: Plan, rank: int, lr: float, beta1: float, beta2: float, eps: float,
                    grad_scale: float, t: int, slices: Optional[GradSrc], reduced, master, m, v,
                    param_dst, param_dt: int, dst_is_full: bool, stream=None) -> None:
+    S = plan.shard_total
+    if slices is not None:
+        slices.check(plan)
+        red = 0
+    else:
+        red = _arg(reduced, "reduced", 4, S)
+    w_, m_, v_ = _arg(master, "master", 4, S), _arg(m, "m", 4, S), _arg(v, "v", 4, S)
+    if param_dt not in (ZERO_F16, ZERO_BF16):
+        raise ValueError(f"parameter dtype {param_dt} is not 16-bit")
+    dst = _arg(param_dst, "param_dst", 2, plan.psi_pad if dst_is_full else S)
     hp = _AdamHyper(lr, beta1, beta2, eps, grad_scale)
     _check(load().zero_adam_step(plan.handle, rank, ctypes.byref(hp), t,
-                                 None if slices is None else ctypes.byref(slices.c), _addr(reduced),
-                                 _addr(master), _addr(m), _addr(v), _addr(param_dst), param_dt,
-                                 1 if dst_is_full else 0, _stream(stream)))
+                                 None if slices is None else ctypes.byref(slices.c), red,
+                                 w_, m_, v_, dst, param_dt, 1 if dst_is_full else 0, _stream(stream)))
 
 
 def zero_gather_pack(plan: Plan, shards: Sequence, dt: int, full, stream=None) -> None:
-    _check(load().zero_gather_pack(plan.handle, _ptr_array(shards), dt, _addr(full), _stream(stream)))
+    es = _esize(dt)
+    arr = _arg_list(shards, "shards", plan.n_d, es, plan.shard_total)
+    out = _arg(full, "full", es, plan.psi_pad)
+    _check(load().zero_gather_pack(plan.handle, arr, dt, out, _stream(stream)))
 
 
 def zero_reshard(src_plan: Plan, dst_plan: Plan, dst_rank: int, src_shards: Sequence, dt: int, dst_shard,
                  stream=None) -> None:
-    _check(load().zero_reshard(src_plan.handle, dst_plan.handle, dst_rank, _ptr_array(src_shards), dt,
-                               _addr(dst_shard), _stream(stream)))
+    es = _esize(dt)
+    arr = _arg_list(src_shards, "src_shards", src_plan.n_d, es, src_plan.shard_total)
+    out = _arg(dst_shard, "dst_shard", es, dst_plan.shard_total)
+    _check(load().zero_reshard(src_plan.handle, dst_plan.handle, dst_rank, arr, dt, out, _stream(stream)))

@@ -24,28 +24,53 @@ from . import ZERO_F32, Plan, zero_plan, zero_reshard
 FORMAT = "zero-shard-state-v1"
 
 
+def _plan_meta(plan_args: Dict) -> Dict:
+    return {k: (list(map(int, plan_args[k])) if k == "tensor_numel" else int(plan_args[k]))
+            for k in ("psi", "n_d", "tensor_numel", "bucket_cap", "shard_align")}
+
+
+def _check_state(name: str, a: np.ndarray, shard_total: int, where: str) -> None:
+    if a.dtype != np.float32:
+        raise ValueError(f"{where}: {name} is {a.dtype}, expected float32")
+    if a.ndim != 1:
+        raise ValueError(f"{where}: {name} has shape {a.shape}, expected one dimension")
+    if a.size != shard_total:
+        raise ValueError(f"{where}: {name} holds {a.size} elements, the plan's shard has {shard_total}")
+
+
 def save_shard(path: str, plan_args: Dict, rank: int, t: int, master, m, v) -> None:
     """Write rank's state.  plan_args: dict(psi, n_d, tensor_numel, bucket_cap,
     shard_align) -- the arguments the shard's plan was built from.  master, m,
-    v: fp32 tensors (any device) of the plan's shard_total elements."""
-    meta = {"format": FORMAT, "rank": int(rank), "t": int(t),
-            "plan": {k: (list(map(int, plan_args[k])) if k == "tensor_numel" else int(plan_args[k]))
-                     for k in ("psi", "n_d", "tensor_numel", "bucket_cap", "shard_align")}}
+    v: one-dimensional fp32 tensors or arrays (any device) of exactly the
+    plan's shard_total elements; anything else raises ValueError and writes
+    nothing."""
+    meta = {"format": FORMAT, "rank": int(rank), "t": int(t), "plan": _plan_meta(plan_args)}
+    S = plan_from(meta["plan"]).shard_total
+    if not 0 <= meta["rank"] < meta["plan"]["n_d"]:
+        raise ValueError(f"rank {rank} outside [0, {meta['plan']['n_d']})")
+    if meta["t"] < 0:
+        raise ValueError(f"step {t} is negative")
     arrays = {}
     for name, x in (("master", master), ("m", m), ("v", v)):
         a = x.detach().cpu().numpy() if hasattr(x, "detach") else np.asarray(x)
-        if a.dtype != np.float32:
-            raise ValueError(f"{name} must be fp32")
+        _check_state(name, a, S, path)
         arrays[name] = np.ascontiguousarray(a)
     np.savez(path, meta=np.frombuffer(json.dumps(meta).encode(), dtype=np.uint8), **arrays)
 
 
 def load_shard(path: str) -> Dict:
+    """Read one rank's file.  Its arrays must be one-dimensional float32 of
+    the shard size its own plan gives; anything else raises ValueError."""
     with np.load(path, allow_pickle=False) as z:
         meta = json.loads(bytes(z["meta"]).decode())
         if meta.get("format") != FORMAT:
             raise ValueError(f"{path}: not a {FORMAT} file")
-        meta.update({k: z[k].copy() for k in ("master", "m", "v")})
+        meta["plan"] = _plan_meta(meta["plan"])
+        S = plan_from(meta["plan"]).shard_total
+        for k in ("master", "m", "v"):
+            a = z[k]
+            _check_state(k, a, S, path)
+            meta[k] = a.copy()
     return meta
 
 
@@ -67,6 +92,9 @@ def restore(paths: Sequence[str], new_plan: Plan, new_rank: int, device="cuda"):
     if sorted(by_rank) != list(range(old_args["n_d"])):
         raise ValueError(f"need one file per old rank 0..{old_args['n_d'] - 1}")
     old_plan = plan_from(old_args)
+    for s in shards:   # already checked by load_shard; kept next to the GPU copies it guards
+        for name in ("master", "m", "v"):
+            _check_state(name, s[name], old_plan.shard_total, f"rank {s['rank']}")
     out = []
     for name in ("master", "m", "v"):
         src = [torch.from_numpy(by_rank[r][name]).to(device) for r in range(old_args["n_d"])]

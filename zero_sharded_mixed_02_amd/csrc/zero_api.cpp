@@ -15,14 +15,16 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <new>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "zero.h"
 #include "zero_internal.h"
 
-#define ZERO_VERSION_NUMBER 101  // 0.1.1
+#define ZERO_VERSION_NUMBER 200  // 0.2.0
 
 struct zero_plan_s {
   int64_t psi = 0;
@@ -111,18 +113,59 @@ std::vector<Piece> owner_pieces(const zero_plan_s& p, int32_t rank, bool dst_ful
   return out;
 }
 
-bool pieces_vectorisable(const std::vector<Piece>& ps) {
-  for (const auto& q : ps)
-    if ((q.shard_off | q.full_off | q.dst_off | q.len) & 7) return false;
-  return true;
+// Pieces for the vector kernel and for the element kernel.  The vector kernel
+// needs every offset it addresses -- the shard offset (state, compact
+// gradients, reduced gradient), the destination offset and, where a rank
+// reads a full buffer, the full offset -- to be a multiple of 4 elements; its
+// length is free.  A piece whose offsets agree modulo 4 gives its first
+// (< 4) elements to the element kernel and the rest to the vector kernel;
+// one whose offsets disagree modulo 4 goes to the element kernel whole.
+void split_pieces(const std::vector<Piece>& ps, bool uses_full, bool uses_dst, std::vector<Piece>& vec,
+                  std::vector<Piece>& elem) {
+  for (const auto& q : ps) {
+    const int64_t r = q.shard_off & 3;
+    const bool agree = (!uses_dst || (q.dst_off & 3) == r) && (!uses_full || (q.full_off & 3) == r);
+    if (!agree) {
+      elem.push_back(q);
+      continue;
+    }
+    const int64_t head = std::min<int64_t>((4 - r) & 3, q.len);
+    if (head > 0) elem.push_back(Piece{q.shard_off, q.full_off, q.dst_off, head});
+    if (q.len > head) vec.push_back(Piece{q.shard_off + head, q.full_off + head, q.dst_off + head, q.len - head});
+  }
 }
 
 int ndc_for(int n) { return (n == 4 || n == 8 || n == 16 || n == 64) ? n : 0; }
 
 // Write-window setting: period in the high 32 bits, open ticks in the low 32;
 // kWindowAuto = automatic.  One word, so a reader never sees a torn pair.
+// The process-wide default, and per-stream settings that override it.
 constexpr uint64_t kWindowAuto = ~0ull;
 std::atomic<uint64_t> g_window{kWindowAuto};
+std::mutex g_stream_window_mu;
+std::vector<std::pair<void*, uint64_t>> g_stream_window;   // guarded by g_stream_window_mu
+std::atomic<int> g_stream_window_count{0};                 // entries, read without the lock
+
+uint64_t window_setting(void* stream) {
+  if (g_stream_window_count.load(std::memory_order_acquire) > 0) {
+    std::lock_guard<std::mutex> lk(g_stream_window_mu);
+    for (const auto& e : g_stream_window)
+      if (e.first == stream) return e.second;
+  }
+  return g_window.load(std::memory_order_relaxed);
+}
+
+// Encodes a (period, open) request; false if out of range.
+bool encode_window(int64_t period_ticks, int64_t open_ticks, uint64_t& w) {
+  if (period_ticks == -1) {
+    w = kWindowAuto;
+    return true;
+  }
+  if (period_ticks < 0 || period_ticks > (int64_t)zk::kMaxWindowPeriod) return false;
+  if (period_ticks > 0 && (open_ticks < 1 || open_ticks > period_ticks)) return false;
+  w = period_ticks == 0 ? 0 : ((uint64_t)period_ticks << 32) | (uint64_t)open_ticks;
+  return true;
+}
 
 // Automatic choice.  A wave waits at most one period, so the period must stay
 // well below the lifetime of a workgroup, or every generation of resident
@@ -134,35 +177,41 @@ std::atomic<uint64_t> g_window{kWindowAuto};
 // Launches with few ranks per written element or few elements gain nothing.
 // A launch of only a few generations (a Stage-3 layer is three) does better
 // with a proportionally shorter period: its waits at the end are not hidden
-// by later generations.
+// by later generations.  The streaming rate is a fixed share of the HBM peak
+// the device reports (memory clock x 4 transfers x bus width: 8.19 TB/s on
+// MI355X, 5.3 TB/s on MI300X), and periods are converted to ticks with the
+// rate the device reports for its real-time counter.
 constexpr int kAutoMinRanks = 16;
 constexpr double kAutoFullGenerations = 6.0;
 constexpr int64_t kAutoMinElems = int64_t(1) << 23;
-constexpr double kAutoStreamBps = 6.5e12;
-constexpr double kTickSeconds = 1e-8;   // real-time counter: 100 MHz
+constexpr double kAutoStreamShare = 6.5e12 / 8.192e12;   // 6.5 TB/s on MI355X
 
 void auto_window(int mode, int gdt, int pdt, int ndc, int n_ranks, int64_t elems, int64_t blocks,
                  zk::StepArgs& a) {
   if (n_ranks < kAutoMinRanks || elems < kAutoMinElems) return;
   const int resident = zk::resident_blocks(mode, gdt, pdt, ndc, true);
   if (resident <= 0 || blocks < 2 * (int64_t)resident) return;
+  const double hz = zk::wall_clock_hz();
+  const double peak = zk::hbm_peak_bps();
+  if (!(hz > 0) || !(peak > 0)) return;
   const double read = 2.0 * n_ranks + (mode == zk::kFused ? 12.0 : (a.flags & zk::kFlagInitFromOut) ? 4.0 : 0.0);
   const double written = mode == zk::kFused ? 14.0 : 4.0;
   const double gen_bytes = (double)resident * zk::kStepThreads * zk::kStepVec * (read + written);
-  double period = gen_bytes / kAutoStreamBps / 2.0 / kTickSeconds;
+  double period = gen_bytes / (kAutoStreamShare * peak) / 2.0 * hz;
   period *= std::min(1.0, (double)blocks / resident / kAutoFullGenerations);
-  period = std::min<double>(std::max(period, 200.0), (double)zk::kMaxWindowPeriod);
+  const double min_period = 2e-6 * hz;   // 2 us
+  period = std::min<double>(std::max(period, min_period), (double)zk::kMaxWindowPeriod);
   const double open = period * std::max(written / (read + written), 1.0 / 16.0);
   a.win_period = (uint32_t)period;
   a.win_open = std::max<uint32_t>(1, std::min<uint32_t>((uint32_t)open, a.win_period));
 }
 
 void pick_window(int mode, int gdt, int pdt, int ndc, int n_ranks, int64_t elems, int64_t blocks, bool vec,
-                 zk::StepArgs& a) {
+                 void* stream, zk::StepArgs& a) {
   a.win_period = 0;
   a.win_open = 0;
   if (!vec || mode == zk::kFromReduced) return;
-  const uint64_t w = g_window.load(std::memory_order_relaxed);
+  const uint64_t w = window_setting(stream);
   if (w != kWindowAuto) {
     a.win_period = (uint32_t)(w >> 32);
     a.win_open = (uint32_t)w;
@@ -195,11 +244,24 @@ zero_status run_step(zk::StepArgs& a, const std::vector<Piece>& ps, int mode, in
     }
     a.n_seg = nseg;
     if (blocks == 0) continue;
-    pick_window(mode, gdt, pdt, ndc_for(a.n_ranks), a.n_ranks, elems, blocks, vec, a);
+    pick_window(mode, gdt, pdt, ndc_for(a.n_ranks), a.n_ranks, elems, blocks, vec, stream, a);
     const int err = zk::launch_step(a, mode, gdt, pdt, ndc_for(a.n_ranks), vec, (int)blocks, stream);
     if (err != 0) return hip_fail(err);
   }
   return ok();
+}
+
+// The step over the owner's pieces: the vector kernel where the buffers
+// allow it (fp32 bases 16-byte aligned, 16-bit bases 8-byte aligned; offsets
+// as split_pieces requires), the element kernel for the rest.  The two sets
+// of pieces are disjoint.
+zero_status run_step_all(zk::StepArgs& a, const std::vector<Piece>& ps, int mode, int gdt, int pdt,
+                         bool vec_ok, bool uses_full, void* stream) {
+  if (!vec_ok) return run_step(a, ps, mode, gdt, pdt, false, stream);
+  std::vector<Piece> vec, elem;
+  split_pieces(ps, uses_full, mode != zk::kReduceOnly, vec, elem);
+  if (zero_status st = run_step(a, vec, mode, gdt, pdt, true, stream)) return st;
+  return run_step(a, elem, mode, gdt, pdt, false, stream);
 }
 
 // Fill the rank table of a step launch with ranks [q0, q0 + n).
@@ -215,7 +277,7 @@ void set_ranks(zk::StepArgs& a, const zero_grad_src& src, int q0, int n) {
 
 // Common checks of a gradient source; collects the read ranges.
 zero_status check_src(const zero_plan_s& p, const zero_grad_src* src, std::vector<Range>& reads,
-                      bool& all16aligned) {
+                      bool& vec_ok) {
   if (!src) return fail(ZERO_EINVAL, "gradient source is NULL");
   if (src->n != p.n_d) return fail(ZERO_EINVAL, "gradient source has %d ranks, plan has n_d=%d", src->n, p.n_d);
   if (!src->ptrs) return fail(ZERO_EINVAL, "gradient pointer array is NULL");
@@ -226,7 +288,7 @@ zero_status check_src(const zero_plan_s& p, const zero_grad_src* src, std::vecto
     const int64_t n = full ? p.psi_pad : p.shard_total;
     if (!g && n > 0) return fail(ZERO_EINVAL, "gradient pointer of rank %d is NULL", q);
     if (!aligned(g, 2)) return fail(ZERO_EINVAL, "gradient of rank %d is not 2-byte aligned", q);
-    if (!aligned(g, 16)) all16aligned = false;
+    if (!aligned(g, 8)) vec_ok = false;   // the vector kernel loads 4 elements (8 bytes) per rank
     reads.push_back(range_of(g, n, 2, "gradient"));
   }
   return ok();
@@ -276,17 +338,37 @@ extern "C" {
 int32_t zero_version(void) { return ZERO_VERSION_NUMBER; }
 
 zero_status zero_set_write_window(int64_t period_ticks, int64_t open_ticks) {
-  if (period_ticks == -1) {
-    g_window.store(kWindowAuto);
-    return ok();
-  }
-  if (period_ticks < 0 || period_ticks > (int64_t)zk::kMaxWindowPeriod)
-    return fail(ZERO_EINVAL, "period_ticks must be -1 or in [0, %u] (got %lld)", zk::kMaxWindowPeriod,
-                (long long)period_ticks);
-  if (period_ticks > 0 && (open_ticks < 1 || open_ticks > period_ticks))
-    return fail(ZERO_EINVAL, "open_ticks must be in [1, period_ticks] (got %lld)", (long long)open_ticks);
-  g_window.store(period_ticks == 0 ? 0 : ((uint64_t)period_ticks << 32) | (uint64_t)open_ticks);
+  uint64_t w = 0;
+  if (!encode_window(period_ticks, open_ticks, w))
+    return fail(ZERO_EINVAL, "window (%lld, %lld): period_ticks must be -1 or in [0, %u], open_ticks in [1, period_ticks]",
+                (long long)period_ticks, (long long)open_ticks, zk::kMaxWindowPeriod);
+  g_window.store(w);
   return ok();
+}
+
+zero_status zero_set_stream_write_window(void* stream, int64_t period_ticks, int64_t open_ticks) {
+  try {
+    std::lock_guard<std::mutex> lk(g_stream_window_mu);
+    auto it = std::find_if(g_stream_window.begin(), g_stream_window.end(),
+                           [&](const std::pair<void*, uint64_t>& e) { return e.first == stream; });
+    if (period_ticks == -2) {   // back to the process-wide setting
+      if (it != g_stream_window.end()) g_stream_window.erase(it);
+    } else {
+      uint64_t w = 0;
+      if (!encode_window(period_ticks, open_ticks, w))
+        return fail(ZERO_EINVAL,
+                    "window (%lld, %lld): period_ticks must be -2, -1 or in [0, %u], open_ticks in [1, period_ticks]",
+                    (long long)period_ticks, (long long)open_ticks, zk::kMaxWindowPeriod);
+      if (it != g_stream_window.end()) it->second = w;
+      else g_stream_window.emplace_back(stream, w);
+    }
+    g_stream_window_count.store((int)g_stream_window.size(), std::memory_order_release);
+    return ok();
+  } catch (const std::bad_alloc&) {
+    return fail(ZERO_ENOMEM, "host allocation failed");
+  } catch (...) {
+    return fail(ZERO_EINVAL, "unexpected failure in zero_set_stream_write_window");
+  }
 }
 
 const char* zero_last_error(void) { return g_err.c_str(); }
@@ -325,8 +407,19 @@ zero_status zero_plan(int64_t psi, int32_t n_d, const int64_t* tensor_numel, int
     // would take it past the cap.
     int64_t flat = 0, shard = 0, open_numel = 0;
     bool open = false;
+    // The padded layout must stay addressable in bytes for fp32 buffers:
+    // psi_pad * 4 <= INT64_MAX.  Each bucket adds less than `unit` padding,
+    // so the check runs before every addition.
+    constexpr int64_t kMaxPadded = INT64_MAX / 4;
+    bool too_big = false;
     auto close_bucket = [&]() {
-      const int64_t padded = (open_numel + unit - 1) / unit * unit;
+      const int64_t rem = open_numel % unit;
+      const int64_t pad = rem ? unit - rem : 0;
+      if (open_numel > kMaxPadded - flat || pad > kMaxPadded - flat - open_numel) {
+        too_big = true;
+        return;
+      }
+      const int64_t padded = open_numel + pad;
       const int64_t sn = padded / n_d;
       p->buckets.push_back({flat, open_numel, padded, sn, shard});
       flat += padded;
@@ -334,15 +427,21 @@ zero_status zero_plan(int64_t psi, int32_t n_d, const int64_t* tensor_numel, int
       open = false;
       open_numel = 0;
     };
-    for (int32_t t = 0; t < n_tensors; ++t) {
+    for (int32_t t = 0; t < n_tensors && !too_big; ++t) {
       const int64_t n = tensor_numel[t];
       if (open && bucket_cap > 0 && open_numel + n > bucket_cap) close_bucket();
+      if (too_big) break;
       p->t_bucket[t] = (int32_t)p->buckets.size();
       p->t_off[t] = flat + open_numel;
       open_numel += n;
       open = true;
     }
-    if (open) close_bucket();
+    if (open && !too_big) close_bucket();
+    if (too_big) {
+      delete p;
+      return fail(ZERO_EINVAL, "padded layout exceeds %lld elements (n_d * shard_align = %lld per bucket)",
+                  (long long)kMaxPadded, (long long)unit);
+    }
     p->psi_pad = flat;
     p->shard_total = shard;
     *out = p;
@@ -387,9 +486,13 @@ zero_status zero_plan_tensor(zero_plan_t p, int32_t t, int32_t* bucket, int64_t*
   return ok();
 }
 
+size_t zero_flatten_workspace_bytes(zero_plan_t) { return 0; }
+
 zero_status zero_flatten(zero_plan_t p, const void* const* tensors, zero_dtype dt, void* flat,
-                         void* stream) {
+                         void* workspace, size_t ws_bytes, void* stream) {
   try {
+    (void)workspace;
+    (void)ws_bytes;   // zero_flatten_workspace_bytes() is 0 for every plan
     if (check_plan(p)) return ZERO_EINVAL;
     if (!valid_dt(dt)) return fail(ZERO_EINVAL, "unknown dtype %d", (int)dt);
     const int es = esize(dt);
@@ -512,17 +615,17 @@ zero_status zero_shard_reduce(zero_plan_t p, int32_t rank, const zero_grad_src* 
     if (check_plan(p)) return ZERO_EINVAL;
     if (rank < 0 || rank >= p->n_d) return fail(ZERO_EINVAL, "rank %d outside [0, %d)", rank, p->n_d);
     std::vector<Range> reads;
-    bool al16 = true;
-    if (zero_status st = check_src(*p, src, reads, al16)) return st;
+    bool vec_ok = true;   // base alignment the vector kernel needs
+    if (zero_status st = check_src(*p, src, reads, vec_ok)) return st;
     if (!out && p->shard_total > 0) return fail(ZERO_EINVAL, "out is NULL");
     if (!aligned(out, 4)) return fail(ZERO_EINVAL, "out is not 4-byte aligned");
-    if (!aligned(out, 16)) al16 = false;
+    if (!aligned(out, 16)) vec_ok = false;
     const Range w = range_of(out, p->shard_total, 4, "out");
     for (const auto& r : reads)
       if (overlap(w, r)) return fail(ZERO_EINVAL, "out overlaps a gradient buffer");
 
     const std::vector<Piece> ps = owner_pieces(*p, rank, false);
-    const bool vec = al16 && pieces_vectorisable(ps);
+    const bool uses_full = src->is_full && std::any_of(src->is_full, src->is_full + src->n, [](uint8_t f) { return f != 0; });
     zk::StepArgs a;
     memset(&a, 0, sizeof a);
     a.out = out;
@@ -532,7 +635,8 @@ zero_status zero_shard_reduce(zero_plan_t p, int32_t rank, const zero_grad_src* 
       const int n = std::min(zk::kMaxRanks, p->n_d - q0);
       set_ranks(a, *src, q0, n);
       a.flags = (q0 > 0 ? zk::kFlagInitFromOut : 0) | (q0 + n == p->n_d ? zk::kFlagApplyScale : 0);
-      if (zero_status st = run_step(a, ps, zk::kReduceOnly, src->dtype, ZERO_F16, vec, stream)) return st;
+      if (zero_status st = run_step_all(a, ps, zk::kReduceOnly, src->dtype, ZERO_F16, vec_ok, uses_full, stream))
+        return st;
     }
     return ok();
   } catch (const std::bad_alloc&) {
@@ -555,16 +659,16 @@ zero_status zero_adam_step(zero_plan_t p, int32_t rank, const zero_adam_hyper* h
     const int64_t S = p->shard_total;
     const int64_t dst_elems = dst_is_full ? p->psi_pad : S;
     std::vector<Range> reads;
-    bool al16 = true;
+    bool vec_ok = true;   // base alignment the vector kernel needs
     if (slices) {
       if (p->n_d > zk::kMaxRanks)
         return fail(ZERO_EUNSUPPORTED, "fused step reads at most %d ranks; use zero_shard_reduce and pass reduced",
                     zk::kMaxRanks);
-      if (zero_status st = check_src(*p, slices, reads, al16)) return st;
+      if (zero_status st = check_src(*p, slices, reads, vec_ok)) return st;
     } else {
       if (!reduced && S > 0) return fail(ZERO_EINVAL, "both slices and reduced are NULL");
       if (!aligned(reduced, 4)) return fail(ZERO_EINVAL, "reduced is not 4-byte aligned");
-      if (!aligned(reduced, 16)) al16 = false;
+      if (!aligned(reduced, 16)) vec_ok = false;
       reads.push_back(range_of(reduced, S, 4, "reduced"));
     }
     float* const st_ptr[3] = {master, m, v};
@@ -573,12 +677,12 @@ zero_status zero_adam_step(zero_plan_t p, int32_t rank, const zero_adam_hyper* h
     for (int i = 0; i < 3; ++i) {
       if (!st_ptr[i] && S > 0) return fail(ZERO_EINVAL, "%s is NULL", st_name[i]);
       if (!aligned(st_ptr[i], 4)) return fail(ZERO_EINVAL, "%s is not 4-byte aligned", st_name[i]);
-      if (!aligned(st_ptr[i], 16)) al16 = false;
+      if (!aligned(st_ptr[i], 16)) vec_ok = false;
       writes.push_back(range_of(st_ptr[i], S, 4, st_name[i]));
     }
     if (!param_dst && dst_elems > 0) return fail(ZERO_EINVAL, "param_dst is NULL");
     if (!aligned(param_dst, 2)) return fail(ZERO_EINVAL, "param_dst is not 2-byte aligned");
-    if (!aligned(param_dst, 16)) al16 = false;
+    if (!aligned(param_dst, 8)) vec_ok = false;   // 4 elements (8 bytes) per store
     writes.push_back(range_of(param_dst, dst_elems, 2, "param_dst"));
     for (size_t i = 0; i < writes.size(); ++i) {
       for (size_t j = i + 1; j < writes.size(); ++j)
@@ -589,7 +693,8 @@ zero_status zero_adam_step(zero_plan_t p, int32_t rank, const zero_adam_hyper* h
     }
 
     const std::vector<Piece> ps = owner_pieces(*p, rank, dst_is_full != 0);
-    const bool vec = al16 && pieces_vectorisable(ps);
+    const bool uses_full = slices && slices->is_full &&
+                           std::any_of(slices->is_full, slices->is_full + slices->n, [](uint8_t f) { return f != 0; });
     zk::StepArgs a;
     memset(&a, 0, sizeof a);
     adam_consts(*hp, t, a.c);
@@ -599,11 +704,11 @@ zero_status zero_adam_step(zero_plan_t p, int32_t rank, const zero_adam_hyper* h
     a.dst = param_dst;
     if (slices) {
       set_ranks(a, *slices, 0, p->n_d);
-      return run_step(a, ps, zk::kFused, slices->dtype, param_dt, vec, stream);
+      return run_step_all(a, ps, zk::kFused, slices->dtype, param_dt, vec_ok, uses_full, stream);
     }
     a.reduced = reduced;
     a.n_ranks = 0;
-    return run_step(a, ps, zk::kFromReduced, ZERO_BF16, param_dt, vec, stream);
+    return run_step_all(a, ps, zk::kFromReduced, ZERO_BF16, param_dt, vec_ok, false, stream);
   } catch (const std::bad_alloc&) {
     return fail(ZERO_ENOMEM, "host allocation failed");
   } catch (...) {

@@ -22,11 +22,12 @@ constexpr int kStepVec = 8;                 // elements per lane in the vector s
 constexpr int kCopyUnits = 8;               // 16-byte units per lane in the copy kernel
 
 // Write windows (vector step kernel, fused and reduce-only modes): a wave that
-// has its results ready waits until the device's real-time counter (a
-// constant 100 MHz clock on gfx950) enters the first win_open ticks of a
-// win_period-tick period, then stores.  Stores of the whole device are thereby
-// gathered into short bursts instead of trickling between the gradient reads.
-constexpr uint32_t kMaxWindowPeriod = 100000;    // 1 ms
+// has its results ready waits until the device's constant-rate real-time
+// counter (the rate hipDeviceAttributeWallClockRate reports; 100 MHz on
+// MI355X) enters the first win_open ticks of a win_period-tick period, then
+// stores.  Stores of the whole device are thereby gathered into short bursts
+// instead of trickling between the gradient reads.
+constexpr uint32_t kMaxWindowPeriod = 100000;    // ticks (1 ms at 100 MHz)
 constexpr uint32_t kWindowSpinMax = 1u << 16;    // bound on a wave's wait-loop iterations
 
 // One contiguous piece of the owner's shard (a bucket's slice, or part of it).
@@ -95,5 +96,10 @@ const char* hip_error_string(int err);
 // Workgroups of the chosen step kernel that the current device holds at once
 // (blocks per CU at the kernel's register use x CUs); 0 if unknown.
 int resident_blocks(int mode, int gdt, int pdt, int ndc, bool vec);
+// Ticks per second of the current device's real-time counter; 0 if unknown.
+double wall_clock_hz();
+// Peak HBM bytes per second of the current device from its memory clock and
+// bus width (clock x 4 transfers x width); 0 if unknown.
+double hbm_peak_bps();
 
 }  // namespace zk

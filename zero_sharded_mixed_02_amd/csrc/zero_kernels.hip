@@ -268,11 +268,69 @@ __device__ __forceinline__ void store_groups(float* p, uint32_t ea, uint32_t eb,
   if (vb) st_nt(gaddr<gf32x4*>(p) + (eb >> 2), f32x4{x[4], x[5], x[6], x[7]});
 }
 
-// Vector kernel.  The host takes it only when every segment offset and length
-// is a multiple of 8 elements and every base address is 16-byte aligned; a
-// segment's last wave tile may be partial, in which case a lane's second group
-// can lie past the end: its loads then repeat the first group's addresses
-// (in bounds) and its stores are skipped.
+// One element e of a segment, with the same arithmetic as the vector kernel:
+// scalar loads at any element alignment.  The element kernel runs it for
+// every element; the vector kernel for the last (< 4) elements of a segment
+// whose length is not a multiple of 4.
+template <int MODE, int GDT, int PDT>
+__device__ __forceinline__ void step_one(const StepArgs& a, int64_t shard_off, int64_t full_off,
+                                         int64_t dst_off, uint32_t e) {
+  float g;
+  if constexpr (MODE == kFromReduced) {
+    g = gaddr<const gf32*>(a.reduced)[shard_off + e];
+  } else {
+    const int n = a.n_ranks;
+    float acc;
+    int q = 0;
+    if (MODE == kReduceOnly && (a.flags & kFlagInitFromOut)) {
+      acc = gaddr<const gf32*>(a.out)[shard_off + e];
+    } else {
+      acc = widen1<GDT>(gaddr<const gu16*>(rank_base(a, 0, shard_off, full_off))[e]);
+      q = 1;
+    }
+    for (; q < n; ++q)
+      acc = acc + widen1<GDT>(gaddr<const gu16*>(rank_base(a, q, shard_off, full_off))[e]);
+    if (MODE == kReduceOnly) {
+      if (a.flags & kFlagApplyScale) acc = acc * a.c[8];
+      gaddr<gf32*>(a.out)[shard_off + e] = acc;
+      return;
+    }
+    g = acc * a.c[8];
+  }
+  if constexpr (MODE != kReduceOnly) {
+    const AdamC k = load_consts(a);
+    gf32* wp = gaddr<gf32*>(a.master);
+    gf32* mp = gaddr<gf32*>(a.m);
+    gf32* vp = gaddr<gf32*>(a.v);
+    float w = wp[shard_off + e], m = mp[shard_off + e], v = vp[shard_off + e];
+    adam1(k, g, w, m, v);
+    wp[shard_off + e] = w;
+    mp[shard_off + e] = m;
+    vp[shard_off + e] = v;
+    gaddr<gu16*>(a.dst)[dst_off + e] = (uint16_t)narrow1<PDT>(w);
+  }
+}
+
+// Element kernel: one element per lane, any element alignment (taken for
+// pieces whose offsets are not multiples of 4 elements, or when a base
+// address is not 16-byte aligned).
+template <int MODE, int GDT, int PDT>
+__global__ void __launch_bounds__(kThreads) step_elem_kernel(const StepArgs a) {
+  const int blk = blockIdx.x;
+  const int s = find_seg(a, blk);
+  const uint32_t len = (uint32_t)a.seg[s].len;
+  const uint32_t e = (uint32_t)(blk - a.seg[s].block_start) * kThreads + threadIdx.x;
+  if (e >= len) return;
+  step_one<MODE, GDT, PDT>(a, a.seg[s].shard_off, a.seg[s].full_off, a.seg[s].dst_off, e);
+}
+
+// Vector kernel.  The host takes it only when a segment's offsets (shard,
+// full-buffer where a rank reads one, destination) are multiples of 4
+// elements and every base address is 16-byte aligned; the length is free.  A
+// segment's last wave tile may be partial: a lane whose second group lies
+// past the end loads the first group's addresses again (in bounds) and skips
+// those stores, and the last (< 4) elements of a length that is not a
+// multiple of 4 go through the element routine.
 template <int MODE, int GDT, int PDT, int NDC>
 __global__ void __launch_bounds__(kStepThreads) step_vec_kernel(const StepArgs a) {
   const int blk = blockIdx.x;
@@ -286,7 +344,12 @@ __global__ void __launch_bounds__(kStepThreads) step_vec_kernel(const StepArgs a
                         (threadIdx.x >> 6) * kTile;
   const uint32_t ea = tile + 4u * lane;
   if (ea >= len) return;
-  const bool vb = ea + kHalf < len;
+  if (ea + 4u > len) {   // the segment's partial last group
+    for (uint32_t e = ea; e < len; ++e) step_one<MODE, GDT, PDT>(a, shard_off, full_off, dst_off, e);
+    return;
+  }
+  const bool vb = ea + kHalf + 4u <= len;        // second group whole
+  const bool tb = !vb && ea + kHalf < len;       // second group partial
   const uint32_t eb = vb ? ea + kHalf : ea;
 
   float g[8];
@@ -340,57 +403,10 @@ __global__ void __launch_bounds__(kStepThreads) step_vec_kernel(const StepArgs a
     st_nt(dp + (ea >> 2), pa);
     if (vb) st_nt(dp + (eb >> 2), pb);
   }
+  if (tb)
+    for (uint32_t e = ea + kHalf; e < len; ++e) step_one<MODE, GDT, PDT>(a, shard_off, full_off, dst_off, e);
 }
 
-// Element kernel: one element per lane, any element alignment (taken when a
-// plan's offsets are not multiples of 8 elements or a base is not 16-byte
-// aligned).
-template <int MODE, int GDT, int PDT>
-__global__ void __launch_bounds__(kThreads) step_elem_kernel(const StepArgs a) {
-  const int blk = blockIdx.x;
-  const int s = find_seg(a, blk);
-  const int64_t shard_off = a.seg[s].shard_off;
-  const int64_t full_off = a.seg[s].full_off;
-  const int64_t dst_off = a.seg[s].dst_off;
-  const uint32_t len = (uint32_t)a.seg[s].len;
-  const uint32_t e = (uint32_t)(blk - a.seg[s].block_start) * kThreads + threadIdx.x;
-  if (e >= len) return;
-
-  float g;
-  if constexpr (MODE == kFromReduced) {
-    g = gaddr<const gf32*>(a.reduced)[shard_off + e];
-  } else {
-    const int n = a.n_ranks;
-    float acc;
-    int q = 0;
-    if (MODE == kReduceOnly && (a.flags & kFlagInitFromOut)) {
-      acc = gaddr<const gf32*>(a.out)[shard_off + e];
-    } else {
-      acc = widen1<GDT>(gaddr<const gu16*>(rank_base(a, 0, shard_off, full_off))[e]);
-      q = 1;
-    }
-    for (; q < n; ++q)
-      acc = acc + widen1<GDT>(gaddr<const gu16*>(rank_base(a, q, shard_off, full_off))[e]);
-    if (MODE == kReduceOnly) {
-      if (a.flags & kFlagApplyScale) acc = acc * a.c[8];
-      gaddr<gf32*>(a.out)[shard_off + e] = acc;
-      return;
-    }
-    g = acc * a.c[8];
-  }
-  if constexpr (MODE != kReduceOnly) {
-    const AdamC k = load_consts(a);
-    gf32* wp = gaddr<gf32*>(a.master);
-    gf32* mp = gaddr<gf32*>(a.m);
-    gf32* vp = gaddr<gf32*>(a.v);
-    float w = wp[shard_off + e], m = mp[shard_off + e], v = vp[shard_off + e];
-    adam1(k, g, w, m, v);
-    wp[shard_off + e] = w;
-    mp[shard_off + e] = m;
-    vp[shard_off + e] = v;
-    gaddr<gu16*>(a.dst)[dst_off + e] = (uint16_t)narrow1<PDT>(w);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Copies (flatten, gather_pack)
@@ -610,6 +626,38 @@ int resident_blocks(int mode, int gdt, int pdt, int ndc, bool vec) {
   r = per_cu * cus;
   slot.store(r > 0 ? r : -1, std::memory_order_relaxed);
   return r > 0 ? r : 0;
+}
+
+namespace {
+// A positive integer attribute of the current device, cached per device and
+// attribute slot; 0 if it cannot be read.
+int device_attribute(int slot_id, hipDeviceAttribute_t attr) {
+  constexpr int kDevices = 64, kSlots = 3;
+  static std::atomic<int> cache[kDevices][kSlots];   // 0 = not yet known, -1 = query failed
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  std::atomic<int>* slot = dev >= 0 && dev < kDevices && slot_id < kSlots ? &cache[dev][slot_id] : nullptr;
+  int v = slot ? slot->load(std::memory_order_relaxed) : 0;
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, attr, dev) != hipSuccess || v <= 0) {
+      (void)hipGetLastError();
+      v = -1;
+    }
+    if (slot) slot->store(v, std::memory_order_relaxed);
+  }
+  return v > 0 ? v : 0;
+}
+}  // namespace
+
+double wall_clock_hz() { return 1e3 * device_attribute(0, hipDeviceAttributeWallClockRate); }
+
+double hbm_peak_bps() {
+  const double khz = device_attribute(1, hipDeviceAttributeMemoryClockRate);
+  const double bits = device_attribute(2, hipDeviceAttributeMemoryBusWidth);
+  return 1e3 * khz * 4.0 * bits / 8.0;
 }
 
 const char* hip_error_string(int err) { return hipGetErrorString((hipError_t)err); }
