@@ -295,7 +295,7 @@ FILL_ORDER_VARIANTS = ("after_step", "after_gradient_fill", "after_gradient_zero
 
 def _predecessor(torch, run, variant, spare, t):
     """Issue the predecessor `variant` of the step on the current stream."""
-    g = run.layers[0]["compact"]
+    g = run.layers[0]["compact_rows"]
     if variant == "after_step":
         run.step(t)
     elif variant == "after_gradient_fill":
@@ -305,7 +305,7 @@ def _predecessor(torch, run, variant, spare, t):
     elif variant == "after_other_15GB_zero":
         spare.zero_()                                   # 15 GB of plain stores elsewhere
     elif variant == "after_gradient_copy":
-        spare.copy_(g.view(-1)[:spare.numel()])        # 15 GB read + 15 GB written elsewhere
+        spare.copy_(run.layers[0]["compact_rows"].view(-1))   # 15 GB read + 15 GB written elsewhere
     elif variant == "after_gradient_zero_then_64MB_read":
         g.zero_()
         spare[: 32 << 20].sum()                         # 64 MB of plain loads
@@ -323,7 +323,7 @@ def measure_fill_order(torch, reps=6):
     from synth.workloads import WORKLOADS, GpuRun
     run = GpuRun(WORKLOADS["7.5B-stage2"])
     S = run.S
-    spare = torch.empty(run.layers[0]["compact"].numel(), dtype=torch.int16, device="cuda")
+    spare = torch.empty(run.layers[0]["compact_rows"].numel(), dtype=torch.int16, device="cuda")
     run.fill_grads(1)
     t = 1
     for _ in range(3):
@@ -360,7 +360,7 @@ def fill_order_run(torch, variants, count=8):
     warm-up; then `count` per variant in the order given."""
     from synth.workloads import WORKLOADS, GpuRun
     run = GpuRun(WORKLOADS["7.5B-stage2"])
-    spare = torch.empty(run.layers[0]["compact"].numel(), dtype=torch.int16, device="cuda")
+    spare = torch.empty(run.layers[0]["compact_rows"].numel(), dtype=torch.int16, device="cuda")
     run.fill_grads(1)
     t = 1
     for _ in range(3):
@@ -656,6 +656,11 @@ def _counter_means(path, kernel_substr, counter):
     return sum(vals) / len(vals), len(vals)
 
 
+# The fused step's instantiation on the 7.5B workload (fused mode, bf16
+# gradients, fp16 parameters, 64 ranks), as rocprofv3 names it.
+HEADLINE_KERNEL = "step_vec_kernel<0, 2, 1, 64>"
+
+
 def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     """Turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) of
     the fused step and of the plain copy probe into HBM bytes per launch.  The
@@ -666,8 +671,8 @@ def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     cw, _ = _counter_means(copy_write_csv, "copyBuffer", "WRITE_SIZE")
     kf = cf * 1024 / copy_bytes
     kw = cw * 1024 / copy_bytes
-    ff, nf = _counter_means(fetch_csv, "step_vec_kernel", "FETCH_SIZE")
-    fw, nw = _counter_means(write_csv, "step_vec_kernel", "WRITE_SIZE")
+    ff, nf = _counter_means(fetch_csv, HEADLINE_KERNEL, "FETCH_SIZE")
+    fw, nw = _counter_means(write_csv, HEADLINE_KERNEL, "WRITE_SIZE")
     reads, writes = ff * 1024 / kf, fw * 1024 / kw
     rec = {"kernel_source_sha": kernel_source_sha(), "kernel": "step_vec_kernel<0, 2, 1, 64> (fused, bf16 grads, fp16 params)",
            "workload": "7.5B-stage2, N_d=64, S=117187520", "fetch_kib_per_dispatch": ff, "write_kib_per_dispatch": fw,

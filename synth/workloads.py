@@ -133,7 +133,12 @@ class GpuRun:
         for layer in range(cfg.layers):
             L = {}
             compact = [q for q in range(cfg.n_d) if q not in cfg.full_ranks]
-            L["compact"] = torch.empty((len(compact), S), dtype=i16, device=dev)
+            # One row per compact rank, each starting on a 256-byte boundary as a
+            # separately received slice would (a row stride of S elements puts
+            # the rows of an odd-sized shard off the 128-byte memory lines).
+            row = -(-S // 128) * 128
+            L["compact_rows"] = torch.empty((len(compact), row), dtype=i16, device=dev)
+            L["compact"] = L["compact_rows"][:, :S]
             L["full_grads"] = {q: torch.empty(P, dtype=i16, device=dev) for q in cfg.full_ranks}
             L["grads"] = [L["full_grads"][q] if q in cfg.full_ranks
                           else L["compact"][compact.index(q)] for q in range(cfg.n_d)]
@@ -345,7 +350,7 @@ class GpuRun:
     def bytes_resident(self) -> int:
         n = 0
         for L in self.layers:
-            n += L["compact"].numel() * 2 + sum(t.numel() * 2 for t in L["full_grads"].values())
+            n += L["compact_rows"].numel() * 2 + sum(t.numel() * 2 for t in L["full_grads"].values())
             n += 3 * self.S * 4
             if "shards" in L:
                 n += L["shards"].numel() * 2
