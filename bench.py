@@ -291,11 +291,40 @@ def measure_calibration(torch):
 # timed one by one with HIP events (median of several).
 FILL_ORDER_VARIANTS = ("after_step", "after_gradient_fill", "after_gradient_zero", "after_other_15GB_zero",
                        "after_gradient_copy", "after_gradient_zero_then_64MB_read", "after_gradient_zero_then_idle_5ms")
+# Further predecessors for locating the cost (--fill-order-run takes any of
+# these too): non-temporal reads of 256 MB at the head or the tail of the
+# gradient rows (the tail is what the zero wrote last) or of another buffer,
+# a plain read of the head, and a zero of half the gradient rows.
+FILL_ORDER_PROBES = ("after_gradient_zero_then_nt_read_head", "after_gradient_zero_then_nt_read_tail",
+                     "after_gradient_zero_then_nt_read_other", "after_gradient_zero_then_plain_read_head",
+                     "after_gradient_zero_first_half", "after_gradient_zero_second_half",
+                     "after_gradient_zero_then_plain_read_32MB_head", "after_gradient_zero_then_plain_read_64MB_master",
+                     "after_step_then_plain_read_64MB_master", "after_gradient_zero_then_plain_read_row_heads",
+                     "after_step_then_plain_read_row_heads", "after_gradient_zero_then_plain_read_256MB_other")
+_PROBE_BYTES = 256 << 20
+
+
+def _nt_read(torch, buf, byte_off):
+    """Non-temporal read of _PROBE_BYTES of buf from byte_off (the calibration
+    read probe)."""
+    from synth import gpu as SG
+    sink = _nt_read.sink
+    if sink is None:
+        sink = _nt_read.sink = torch.empty(SG.probe_sink_words(_PROBE_BYTES), dtype=torch.int32, device="cuda")
+    nbytes = buf.numel() * buf.element_size()
+    if byte_off < 0 or byte_off + _PROBE_BYTES > nbytes or byte_off % 16:
+        raise ValueError("probe read outside the buffer")
+    SG.probe(SG.PROBE_READ, 0, buf.data_ptr() + byte_off, _PROBE_BYTES, sink.data_ptr(),
+             torch.cuda.current_stream().cuda_stream)
+
+
+_nt_read.sink = None
 
 
 def _predecessor(torch, run, variant, spare, t):
     """Issue the predecessor `variant` of the step on the current stream."""
     g = run.layers[0]["compact_rows"]
+    gb = g.numel() * 2
     if variant == "after_step":
         run.step(t)
     elif variant == "after_gradient_fill":
@@ -305,7 +334,7 @@ def _predecessor(torch, run, variant, spare, t):
     elif variant == "after_other_15GB_zero":
         spare.zero_()                                   # 15 GB of plain stores elsewhere
     elif variant == "after_gradient_copy":
-        spare.copy_(run.layers[0]["compact_rows"].view(-1))   # 15 GB read + 15 GB written elsewhere
+        spare.copy_(g.view(-1))                         # 15 GB read + 15 GB written elsewhere
     elif variant == "after_gradient_zero_then_64MB_read":
         g.zero_()
         spare[: 32 << 20].sum()                         # 64 MB of plain loads
@@ -313,12 +342,47 @@ def _predecessor(torch, run, variant, spare, t):
         g.zero_()
         torch.cuda.synchronize()
         time.sleep(0.005)
+    elif variant == "after_gradient_zero_then_nt_read_head":
+        g.zero_()
+        _nt_read(torch, g, 0)
+    elif variant == "after_gradient_zero_then_nt_read_tail":
+        g.zero_()
+        _nt_read(torch, g, (gb - _PROBE_BYTES) // 16 * 16)
+    elif variant == "after_gradient_zero_then_nt_read_other":
+        g.zero_()
+        _nt_read(torch, spare, 0)
+    elif variant == "after_gradient_zero_then_plain_read_head":
+        g.zero_()
+        g.view(-1)[: _PROBE_BYTES // 2].sum()           # 256 MB of plain loads
+    elif variant == "after_gradient_zero_then_plain_read_32MB_head":
+        g.zero_()
+        g.view(-1)[: 16 << 20].sum()                    # 32 MB of plain loads of the step's own gradients
+    elif variant == "after_gradient_zero_then_plain_read_64MB_master":
+        g.zero_()
+        run.layers[0]["master"][: 16 << 20].sum()       # 64 MB of plain loads of the step's own state
+    elif variant == "after_step_then_plain_read_64MB_master":
+        run.step(t)
+        run.layers[0]["master"][: 16 << 20].sum()
+    elif variant == "after_gradient_zero_then_plain_read_row_heads":
+        g.zero_()
+        g[:, : 2 << 20].sum()                           # first 4 MB of every gradient row (256 MB)
+    elif variant == "after_step_then_plain_read_row_heads":
+        run.step(t)
+        g[:, : 2 << 20].sum()
+    elif variant == "after_gradient_zero_then_plain_read_256MB_other":
+        g.zero_()
+        spare[: 128 << 20].sum()
+    elif variant == "after_gradient_zero_first_half":
+        g[: g.shape[0] // 2].zero_()
+    elif variant == "after_gradient_zero_second_half":
+        g[g.shape[0] // 2:].zero_()
     else:
         raise ValueError(variant)
 
 
 def measure_fill_order(torch, reps=6):
-    """The fused 7.5B step after each predecessor of FILL_ORDER_VARIANTS."""
+    """The fused 7.5B step after each predecessor of FILL_ORDER_VARIANTS and
+    FILL_ORDER_PROBES."""
     import statistics
     from synth.workloads import WORKLOADS, GpuRun
     run = GpuRun(WORKLOADS["7.5B-stage2"])
@@ -332,7 +396,7 @@ def measure_fill_order(torch, reps=6):
     stream = torch.cuda.current_stream()
     out = {}
     nbytes = algorithmic_bytes_per_param(64) * S
-    for variant in FILL_ORDER_VARIANTS:
+    for variant in FILL_ORDER_VARIANTS + FILL_ORDER_PROBES:
         ms = []
         for _ in range(reps):
             t += 1
