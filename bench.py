@@ -671,7 +671,7 @@ def measure_windows(torch):
     return out
 
 
-def _stage3_with_compute(torch, run, t, nl, P, S, tokens=2048):
+def _stage3_with_compute(torch, run, t, nl, P, S, tokens=2048, splits=()):
     import zero_sharded_mixed_02_amd as Z
     h = 8192
     offs = [run.plan.tensor(i)[1] for i in range(len(run.cfg.sizes))]
@@ -708,6 +708,65 @@ def _stage3_with_compute(torch, run, t, nl, P, S, tokens=2048):
         res[name + "_ms"] = _time_launches(torch, loop, reps=5, warmup=2)
     Z.zero_set_write_window(-1)
     res["gather_hidden_fraction"] = (res["serial_ms"] - res["pipelined_ms"]) / res["gather_only_ms"]
+    if splits:
+        res["cu_split"] = _stage3_cu_split(torch, run, t, nl, compute, compute_only, splits)
+    return res
+
+
+def _on(torch, stream, fn):
+    """Run fn with `stream` current, ordered after and before the caller's
+    current stream (so events on the caller's stream bracket it)."""
+    cur = torch.cuda.current_stream()
+    stream.wait_stream(cur)
+    with torch.cuda.stream(stream):
+        fn()
+    cur.wait_stream(stream)
+
+
+def _stage3_cu_split(torch, run, t, nl, compute, compute_only, splits):
+    """The prefetching Stage-3 loop with the compute units split between the
+    streams: the layer compute and the step on n - k CUs, the next layer's
+    gather on the other k ("gather_k") or on any CU ("gather_any"); both sets
+    hold the same share of every die.  Per k also the compute alone on its
+    n - k CUs and the gather alone on its k."""
+    import zero_sharded_mixed_02_amd as Z
+    from synth import gpu as SG
+    n = SG.cu_count()
+    out = {"cus": n}
+    shards = list(run.layers[0]["shards"])
+    for k in splits:
+        g_cus = SG.balanced_cus(k, n)
+        ms_c = SG.MaskedStream(torch, sorted(set(range(n)) - set(g_cus)))
+        ms_g = SG.MaskedStream(torch, g_cus)
+        e = {"compute_only_ms": _time_launches(torch, lambda: _on(torch, ms_c.torch, compute_only), reps=5, warmup=2),
+             "gather_only_ms": nl * _time_launches(
+                 torch, lambda: _on(torch, ms_g.torch, lambda: Z.zero_gather_pack(
+                     run.plan, shards, run.cfg.pdt, run.full, ms_g.torch.cuda_stream)), reps=10, warmup=2)}
+        for name, side in (("gather_k", ms_g.torch), ("gather_any", None)):
+            def loop(side=side):
+                t[0] += 1
+                run.layer_loop(t[0], True, compute, side=side)
+            e[name + "_ms"] = _time_launches(torch, lambda: _on(torch, ms_c.torch, loop), reps=5, warmup=2)
+        ms_c.close()
+        ms_g.close()
+        out[str(k)] = e
+        log(f"stage3 CU split k={k}: " + ", ".join(f"{a} {b:.2f}" for a, b in e.items()))
+    return out
+
+
+def measure_stage3_overlap(torch, splits=(16, 32, 64)):
+    """The Stage-3 8-layer loop with a layer-compute stand-in: serial,
+    prefetching on a second stream, and prefetching with the CUs split."""
+    from synth.workloads import WORKLOADS, GpuRun
+    run = GpuRun(WORKLOADS["stage3-h8192x8"])
+    for layer in range(run.cfg.layers):
+        run.fill_grads(1, layer)
+    t = [1]
+    res = _stage3_with_compute(torch, run, t, run.cfg.layers, run.P, run.S, splits=splits)
+    res["temp_buffer_bytes"] = {"serial": 2 * run.P, "pipelined": 4 * run.P}
+    del run
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     return res
 
 
@@ -856,6 +915,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels", action="store_true",
                     help="also time every entry point at its own workload (adds a 'kernels' object)")
+    ap.add_argument("--stage3-overlap", action="store_true",
+                    help="also time the Stage-3 loop with a compute stand-in, serial, prefetching and with the "
+                         "CUs split between compute and gather (adds 'stage3_overlap')")
     ap.add_argument("--window-sweep", action="store_true",
                     help="also time the step under a grid of write windows (adds a 'write_windows' object)")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -990,7 +1052,10 @@ def main():
         "after_fresh_gradient_fill": {
             "ms_per_step": sum(fresh_ms) / len(fresh_ms), "steps": len(fresh_ms),
             "frac": launch_bytes / (sum(fresh_ms) / len(fresh_ms) / 1e3) / 1e9 / HBM_PEAK_GBPS,
-            "note": "not the timed region: each step right after a fresh 15 GB seeded refill of the gradients"},
+            "note": "not the timed region: each step right after a fresh 15 GB seeded refill of the gradients; "
+                    "stores to the addresses the step then reads leave its waves issuing the same loads more "
+                    "slowly (same L2 and DRAM traffic, lower fabric latency under counters), and a cached read "
+                    "in between removes it"},
     }
     del run
     torch.cuda.synchronize()
@@ -1004,6 +1069,8 @@ def main():
         out["kernels_detail"] = measure_kernels(torch)
     if args.window_sweep:
         out["write_windows"] = measure_windows(torch)
+    if args.stage3_overlap:
+        out["stage3_overlap"] = measure_stage3_overlap(torch)
     if args.no_cpu_baseline or args.headline_only:
         out["cpu_baseline"] = None
     else:

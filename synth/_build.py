@@ -1,12 +1,13 @@
-"""Build step for the GPU half of the synthetic-input generator and the
-benchmark's HBM calibration probes (libsynth.so), and the host half of the
-generator (libsynth_cpu.so)."""
+"""Build step for the GPU half of the synthetic-input generator, the
+benchmark's HBM calibration probes and CU-masked streams (libsynth.so), and
+the host half of the generator (libsynth_cpu.so)."""
 import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "synth_fill.hip")
 PROBE_SRC = os.path.join(HERE, "probes.hip")
+STREAM_SRC = os.path.join(HERE, "streams.hip")
 LIB = os.path.join(HERE, "libsynth.so")
 CPU_SRC = os.path.join(HERE, "synth_cpu.c")
 CPU_LIB = os.path.join(HERE, "libsynth_cpu.so")
@@ -31,7 +32,7 @@ def build(force=True):
     if not force and os.path.exists(LIB):
         return LIB
     tmp = LIB + ".tmp"
-    subprocess.run([HIPCC, *FLAGS, SRC, PROBE_SRC, "-o", tmp], check=True,
+    subprocess.run([HIPCC, *FLAGS, SRC, PROBE_SRC, STREAM_SRC, "-o", tmp], check=True,
                    stderr=subprocess.PIPE if not os.environ.get("ZERO_BUILD_VERBOSE") else None)
     os.replace(tmp, LIB)
     return LIB

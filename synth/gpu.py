@@ -1,6 +1,7 @@
 """ctypes wrapper of libsynth.so: GPU fills of the seeded synthetic inputs
-(definition in synth/__init__.py), and the benchmark's HBM calibration
-probes (plain read, write and copy)."""
+(definition in synth/__init__.py), the benchmark's HBM calibration probes
+(plain read, write and copy), and streams restricted to a set of compute
+units."""
 from __future__ import annotations
 
 import ctypes
@@ -23,6 +24,13 @@ def load():
                                   ctypes.c_void_p, ctypes.c_void_p]
         L.synth_probe_sink_words.restype = ctypes.c_int64
         L.synth_probe_sink_words.argtypes = [ctypes.c_int64]
+        L.synth_cu_count.restype = ctypes.c_int
+        L.synth_cu_count.argtypes = [ctypes.POINTER(ctypes.c_int)]
+        L.synth_stream_create_cu_masked.restype = ctypes.c_int
+        L.synth_stream_create_cu_masked.argtypes = [ctypes.c_uint32, ctypes.POINTER(ctypes.c_uint32),
+                                                    ctypes.POINTER(ctypes.c_void_p)]
+        L.synth_stream_destroy.restype = ctypes.c_int
+        L.synth_stream_destroy.argtypes = [ctypes.c_void_p]
         L.synth_fill.restype = ctypes.c_int
         L.synth_fill.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64,
                                  ctypes.c_uint64, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
@@ -58,3 +66,60 @@ def probe(kind: int, dst: int, src: int, nbytes: int, sink: int, stream: int) ->
                              ctypes.c_void_p(stream))
     if err != 0:
         raise RuntimeError(f"synth_probe({kind}) failed with HIP error {err}")
+
+
+def cu_count() -> int:
+    n = ctypes.c_int(0)
+    err = load().synth_cu_count(ctypes.byref(n))
+    if err != 0:
+        raise RuntimeError(f"synth_cu_count failed with HIP error {err}")
+    return n.value
+
+
+def cu_mask_words(cus, n_cus: int):
+    """32-bit mask words with bit i set for every CU index i in cus."""
+    words = [0] * ((n_cus + 31) // 32)
+    for i in cus:
+        if not 0 <= i < n_cus:
+            raise ValueError(f"CU {i} outside [0, {n_cus})")
+        words[i // 32] |= 1 << (i % 32)
+    return words
+
+
+def balanced_cus(k: int, n_cus: int, n_xcd: int = 8):
+    """k CU indices that give every one of the n_xcd dies the same share,
+    whether the runtime numbers CUs die by die (index // (n_cus / n_xcd)) or
+    round-robin across dies (index % n_xcd): die x takes the indices
+    x * per + ((x + j) % n_xcd) + n_xcd * (j // n_xcd) for j < k / n_xcd.
+    A kernel's workgroups are split across the dies ahead of time, so a set
+    that left a die without CUs would leave that die's workgroups unrun."""
+    per = n_cus // n_xcd
+    if n_cus % n_xcd or per % n_xcd or k % n_xcd or not 0 < k < n_cus:
+        raise ValueError(f"cannot split {k} of {n_cus} CUs evenly over {n_xcd} dies")
+    m = k // n_xcd
+    return sorted(x * per + (x + j) % n_xcd + n_xcd * (j // n_xcd) for x in range(n_xcd) for j in range(m))
+
+
+class MaskedStream:
+    """A HIP stream whose kernels run only on the given CUs, wrapped as a
+    torch external stream (``.torch``).  Default priority."""
+
+    def __init__(self, torch, cus, device=None):
+        n = cu_count()
+        words = cu_mask_words(cus, n)
+        if not any(words):
+            raise ValueError("empty CU mask")
+        arr = (ctypes.c_uint32 * len(words))(*words)
+        h = ctypes.c_void_p()
+        err = load().synth_stream_create_cu_masked(len(words), arr, ctypes.byref(h))
+        if err != 0:
+            raise RuntimeError(f"hipExtStreamCreateWithCUMask failed with HIP error {err}")
+        self.handle = h.value
+        self.cus = sorted(set(cus))
+        self.torch = torch.cuda.ExternalStream(self.handle, device=device)
+
+    def close(self):
+        if self.handle:
+            self.torch.synchronize()
+            load().synth_stream_destroy(ctypes.c_void_p(self.handle))
+            self.handle = None

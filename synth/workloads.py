@@ -218,7 +218,7 @@ class GpuRun:
         Z.zero_adam_step(self.plan, cfg.owner, cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.grad_scale, t,
                          self.src[layer], None, L["master"], L["m"], L["v"], dst, cfg.pdt, dst_full, stream)
 
-    def layer_loop(self, t: int, pipelined: bool = False, compute=None):
+    def layer_loop(self, t: int, pipelined: bool = False, compute=None, side=None):
         """One Stage-3 pass over all layers: for each layer, gather_pack of
         the layer's shards into a full-layer buffer, then the fused step into
         the owner's resident shard.
@@ -230,7 +230,10 @@ class GpuRun:
         pre-step shard, and gather(l+2) reuses a buffer only after step(l)
         (standing in for the layer's compute that reads it) has finished.
         compute(layer, buffer), if given, runs on the current stream between a
-        layer's gather and its step, reading the gathered buffer."""
+        layer's gather and its step, reading the gathered buffer.  side, if
+        given, is the torch stream the pipelined gathers run on (for example
+        one restricted to a set of compute units while the current stream holds
+        the rest); by default a stream of this run's own."""
         torch, Z, cfg = self.torch, self.Z, self.cfg
         if not pipelined:
             for layer in range(cfg.layers):
@@ -241,7 +244,9 @@ class GpuRun:
             self.side = torch.cuda.Stream(device=self.device)
         bufs = [self.full, self.full2]
         main = torch.cuda.current_stream(self.device)
-        side = self.side
+        side = self.side if side is None else side
+        if side == main:
+            raise ValueError("the gather stream must differ from the current stream")
         side.wait_stream(main)
         gathered = [torch.cuda.Event() for _ in range(cfg.layers)]
         stepped = [torch.cuda.Event() for _ in range(cfg.layers)]

@@ -392,6 +392,64 @@ def test_stage3_compute_sees_its_layer(gpu, oracle_lib):
             assert np.array_equal(a["shards"], b["shards"]), (t, layer)
 
 
+@pytest.mark.parametrize("k", [16, 64])
+def test_stage3_cu_split_loop_matches_serial(gpu, oracle_lib, k):
+    """The prefetching loop with the compute units split between streams --
+    layer compute and step on n - k CUs, the next layer's gather on the other
+    k (the same share of every die) -- leaves exactly the serial loop's state,
+    and every layer's compute reads that layer's gathered (pre-step)
+    weights."""
+    import torch
+    from oracle.runner import OracleRun
+    from synth import gpu as SG
+    from synth.workloads import layer_sizes
+    cfg = Config("stage3-cusplit", tuple(layer_sizes(128)), n_d=8, gdt=BF16, pdt=F16, stage=3,
+                 owner=6, steps=2, layers=5, seed=31)
+    n = SG.cu_count()
+    say(f"[stage3] CU split k={k} of {n}, h=128 n_d=8 layers=5 steps=2")
+    if n % 64:
+        pytest.skip(f"{n} CUs do not split evenly over 8 dies")
+    g_cus = SG.balanced_cus(k, n)
+    serial, split, ref = GpuRun(cfg), GpuRun(cfg), OracleRun(cfg)
+    ms_c = SG.MaskedStream(torch, sorted(set(range(n)) - set(g_cus)))
+    ms_g = SG.MaskedStream(torch, g_cus)
+    seen = {name: [torch.empty_like(serial.full) for _ in range(cfg.layers)] for name in ("serial", "split")}
+
+    def recorder(name):
+        def compute(layer, buf):
+            seen[name][layer].copy_(buf)
+        return compute
+
+    try:
+        for t in range(1, cfg.steps + 1):
+            for layer in range(cfg.layers):
+                serial.fill_grads(t, layer)
+                split.fill_grads(t, layer)
+                ref.fill_grads(t, layer)
+            serial.layer_loop(t, pipelined=False, compute=recorder("serial"))
+            cur = torch.cuda.current_stream()
+            ms_c.torch.wait_stream(cur)
+            with torch.cuda.stream(ms_c.torch):
+                split.layer_loop(t, pipelined=True, compute=recorder("split"), side=ms_g.torch)
+            cur.wait_stream(ms_c.torch)
+            for layer in range(cfg.layers):
+                ref.step(t, layer)
+            _sync()
+            for layer in range(cfg.layers):
+                want = ref.state(layer)["gathered"]
+                for name in ("serial", "split"):
+                    got = seen[name][layer].cpu().numpy().view(np.uint16)
+                    assert np.array_equal(got, want), (t, layer, name)
+                a, b = serial.fetch(layer), split.fetch(layer)
+                for key in ("master", "m", "v"):
+                    assert np.array_equal(a[key].view(np.uint32), b[key].view(np.uint32)), (t, layer, key)
+                assert np.array_equal(a["shards"], b["shards"]), (t, layer)
+                assert_state({key: b[key] for key in ("master", "m", "v")}, ref.state(layer), cfg.pdt, f"L{layer}")
+    finally:
+        ms_c.close()
+        ms_g.close()
+
+
 # ---------------------------------------------------------------------------
 # Special values and the output conversion
 # ---------------------------------------------------------------------------

@@ -82,3 +82,34 @@ def test_gpu_fill_matches_host(gpu, dt, mix):
     x = synth.mix_f32(k, ks, pos, 1e-3) if mix else synth.normal_f32(k, pos, 1e-3)
     want = synth.to_dtype_bits(x, dt).view(np.uint32 if dt == synth.F32 else np.uint16)
     assert np.array_equal(got, want)
+
+
+def test_cu_mask_words():
+    """CU index sets -> 32-bit mask words (host logic of the CU-masked streams)."""
+    from synth.gpu import cu_mask_words
+    assert cu_mask_words(range(16), 256) == [0xFFFF, 0, 0, 0, 0, 0, 0, 0]
+    assert cu_mask_words(range(16, 256), 256) == [0xFFFF0000] + [0xFFFFFFFF] * 7
+    assert cu_mask_words([0, 33, 255], 256) == [1, 2, 0, 0, 0, 0, 0, 1 << 31]
+    assert cu_mask_words([], 80) == [0, 0, 0]
+    a, b = cu_mask_words(range(64), 256), cu_mask_words(range(64, 256), 256)
+    assert all(x & y == 0 for x, y in zip(a, b)) and all(x | y == 0xFFFFFFFF for x, y in zip(a, b))
+    with pytest.raises(ValueError):
+        cu_mask_words([256], 256)
+    with pytest.raises(ValueError):
+        cu_mask_words([-1], 256)
+
+
+@pytest.mark.parametrize("k", [8, 16, 32, 64, 128, 248])
+def test_balanced_cus(k):
+    """The CU set of a masked stream, and its complement, give every die the
+    same number of CUs under both numberings (die-major and round-robin)."""
+    from synth.gpu import balanced_cus
+    n, dies = 256, 8
+    a = balanced_cus(k, n, dies)
+    b = sorted(set(range(n)) - set(a))
+    assert len(a) == k and len(set(a)) == k and all(0 <= i < n for i in a)
+    for cus, want in ((a, k // dies), (b, (n - k) // dies)):
+        assert np.bincount([i // (n // dies) for i in cus], minlength=dies).tolist() == [want] * dies
+        assert np.bincount([i % dies for i in cus], minlength=dies).tolist() == [want] * dies
+    with pytest.raises(ValueError):
+        balanced_cus(12, n, dies)
