@@ -147,9 +147,17 @@ def _host_cpu():
     return {"cpu_model": model, "cpus_available": len(os.sched_getaffinity(0))}
 
 
+# GPU cycles of the spin queued before each timed call (about 2 ms): the host
+# marshals and launches the call while the GPU still spins, so the events
+# around the call bracket its kernels and not the host's argument checks
+# (which for the 193-tensor flatten take longer than its kernels).
+_SPIN_CYCLES = 5_000_000
+
+
 def _time_launches(torch, fn, reps=20, warmup=3):
     """Average milliseconds per call of fn (one or more launches on torch's
-    current stream), from HIP events around each call."""
+    current stream), from HIP events around each call, each call queued
+    behind a GPU spin so that host time does not count."""
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         fn()
@@ -157,6 +165,7 @@ def _time_launches(torch, fn, reps=20, warmup=3):
     st = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
     en = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
     for i in range(reps):
+        torch.cuda._sleep(_SPIN_CYCLES)
         st[i].record(stream)
         fn()
         en[i].record(stream)
@@ -1049,6 +1058,9 @@ def main():
                      "algorithmic_bytes_per_launch": launch_bytes,
                      "avg_launch_ms": avg_launch_s * 1e3, "kernel": "step_vec_kernel (fused)"},
         "write_window": "automatic (library default)",
+        # Sustained runs: the mean launch time of each block of 100 timed steps.
+        "per_100_steps_ms": [sum(launch_ms[i:i + 100]) / 100 for i in range(0, len(launch_ms) - 99, 100)]
+        if len(launch_ms) >= 200 else None,
         "after_fresh_gradient_fill": {
             "ms_per_step": sum(fresh_ms) / len(fresh_ms), "steps": len(fresh_ms),
             "frac": launch_bytes / (sum(fresh_ms) / len(fresh_ms) / 1e3) / 1e9 / HBM_PEAK_GBPS,
