@@ -298,7 +298,8 @@ def measure_calibration(torch):
 
 # What runs right before the fused step: each predecessor, then the step,
 # timed one by one with HIP events (median of several).
-FILL_ORDER_VARIANTS = ("after_step", "after_gradient_fill", "after_gradient_zero", "after_other_15GB_zero",
+FILL_ORDER_VARIANTS = ("after_step", "after_gradient_fill", "after_gradient_nt_fill", "after_gradient_zero",
+                       "after_other_15GB_zero",
                        "after_gradient_copy", "after_gradient_zero_then_64MB_read", "after_gradient_zero_then_idle_5ms")
 # Further predecessors for locating the cost (--fill-order-run takes any of
 # these too): non-temporal reads of 256 MB at the head or the tail of the
@@ -309,7 +310,8 @@ FILL_ORDER_PROBES = ("after_gradient_zero_then_nt_read_head", "after_gradient_ze
                      "after_gradient_zero_first_half", "after_gradient_zero_second_half",
                      "after_gradient_zero_then_plain_read_32MB_head", "after_gradient_zero_then_plain_read_64MB_master",
                      "after_step_then_plain_read_64MB_master", "after_gradient_zero_then_plain_read_row_heads",
-                     "after_step_then_plain_read_row_heads", "after_gradient_zero_then_plain_read_256MB_other")
+                     "after_step_then_plain_read_row_heads", "after_gradient_zero_then_plain_read_256MB_other",
+                     "after_gradient_nt_write", "after_gradient_nt_write_then_idle_5ms")
 _PROBE_BYTES = 256 << 20
 
 
@@ -330,6 +332,13 @@ def _nt_read(torch, buf, byte_off):
 _nt_read.sink = None
 
 
+def _nt_write(torch, buf):
+    """Non-temporal stores over all of buf (the calibration write probe)."""
+    from synth import gpu as SG
+    nbytes = buf.numel() * buf.element_size() // 16 * 16
+    SG.probe(SG.PROBE_WRITE, buf.data_ptr(), 0, nbytes, 0, torch.cuda.current_stream().cuda_stream)
+
+
 def _predecessor(torch, run, variant, spare, t):
     """Issue the predecessor `variant` of the step on the current stream."""
     g = run.layers[0]["compact_rows"]
@@ -338,6 +347,8 @@ def _predecessor(torch, run, variant, spare, t):
         run.step(t)
     elif variant == "after_gradient_fill":
         run.fill_grads(t)                               # the seeded generator (ALU-heavy writes)
+    elif variant == "after_gradient_nt_fill":
+        run.fill_grads(t, nt=True)                      # the same values, non-temporal stores
     elif variant == "after_gradient_zero":
         g.zero_()                                       # 15 GB of plain stores over the gradients
     elif variant == "after_other_15GB_zero":
@@ -381,6 +392,11 @@ def _predecessor(torch, run, variant, spare, t):
     elif variant == "after_gradient_zero_then_plain_read_256MB_other":
         g.zero_()
         spare[: 128 << 20].sum()
+    elif variant in ("after_gradient_nt_write", "after_gradient_nt_write_then_idle_5ms"):
+        _nt_write(torch, g)                             # 15 GB of non-temporal stores over the gradients
+        if variant.endswith("idle_5ms"):
+            torch.cuda.synchronize()
+            time.sleep(0.005)
     elif variant == "after_gradient_zero_first_half":
         g[: g.shape[0] // 2].zero_()
     elif variant == "after_gradient_zero_second_half":
@@ -1014,17 +1030,21 @@ def main():
     # Outside the timed region: a few steps each right after a fresh 15 GB
     # gradient fill (plain stores), timed one by one.  A long write-only phase
     # just before the step costs it most of its write-window gain.
-    fresh_ms = []
-    for _ in range(4):
-        t += 1
-        run.fill_grads(t)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        run.step(t)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        fresh_ms.append(e0.elapsed_time(e1))
+    # The fill writes with ordinary (cached) stores, and again with
+    # non-temporal stores, as a streaming receive of the slices would.
+    fresh = {False: [], True: []}
+    for nt in (False, True):
+        for _ in range(4):
+            t += 1
+            run.fill_grads(t, nt=nt)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run.step(t)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            fresh[nt].append(e0.elapsed_time(e1))
+    fresh_ms, fresh_nt_ms = fresh[False], fresh[True]
     ms_per_step = total_ms / args.steps
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
     bpp = algorithmic_bytes_per_param(cfg.n_d)
@@ -1064,10 +1084,14 @@ def main():
         "after_fresh_gradient_fill": {
             "ms_per_step": sum(fresh_ms) / len(fresh_ms), "steps": len(fresh_ms),
             "frac": launch_bytes / (sum(fresh_ms) / len(fresh_ms) / 1e3) / 1e9 / HBM_PEAK_GBPS,
-            "note": "not the timed region: each step right after a fresh 15 GB seeded refill of the gradients; "
-                    "stores to the addresses the step then reads leave its waves issuing the same loads more "
-                    "slowly (same L2 and DRAM traffic, lower fabric latency under counters), and a cached read "
-                    "in between removes it"},
+            "non_temporal_fill": {
+                "ms_per_step": sum(fresh_nt_ms) / len(fresh_nt_ms), "steps": len(fresh_nt_ms),
+                "frac": launch_bytes / (sum(fresh_nt_ms) / len(fresh_nt_ms) / 1e3) / 1e9 / HBM_PEAK_GBPS},
+            "note": "not the timed region: each step right after a fresh 15 GB seeded refill of the gradients, "
+                    "written with ordinary cached stores (ms_per_step) or with non-temporal stores "
+                    "(non_temporal_fill); cached stores to the addresses the step then reads leave its waves "
+                    "issuing the same loads more slowly (same L2 and DRAM traffic, lower fabric latency under "
+                    "counters); non-temporal stores, as the library's own producers use, leave no such cost"},
     }
     del run
     torch.cuda.synchronize()

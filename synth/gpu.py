@@ -34,19 +34,19 @@ def load():
         L.synth_fill.restype = ctypes.c_int
         L.synth_fill.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64,
                                  ctypes.c_uint64, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
-                                 ctypes.c_void_p]
+                                 ctypes.c_int, ctypes.c_void_p]
         _lib = L
     return _lib
 
 
 def fill(addr: int, dt: int, n: int, key: int, pos_base: int, sigma: float, stream: int,
-         mix: bool = False, sel_key: int = 0) -> None:
+         mix: bool = False, sel_key: int = 0, nt: bool = False) -> None:
     """Fill n elements at device address addr with the values at flat
-    positions pos_base .. pos_base + n - 1."""
+    positions pos_base .. pos_base + n - 1 (nt: with non-temporal stores)."""
     if n <= 0:
         return
     err = load().synth_fill(ctypes.c_void_p(addr), dt, n, key, sel_key, 1 if mix else 0, pos_base,
-                            ctypes.c_float(float(scale_for(sigma))), ctypes.c_void_p(stream))
+                            ctypes.c_float(float(scale_for(sigma))), 1 if nt else 0, ctypes.c_void_p(stream))
     if err != 0:
         raise RuntimeError(f"synth_fill failed with HIP error {err}")
 

@@ -83,7 +83,9 @@ __device__ __forceinline__ float value_at(uint64_t key, uint64_t sel_key, int mi
   return x;
 }
 
-template <int DT>
+// NT: store with non-temporal stores (streaming, as a receive of incoming
+// data would) instead of ordinary cached stores; the values are the same.
+template <int DT, bool NT>
 __global__ void __launch_bounds__(256) fill_kernel(void* __restrict__ out, int64_t n, uint64_t key,
                                                    uint64_t sel_key, int mix, int64_t pos_base,
                                                    float scale) {
@@ -91,32 +93,42 @@ __global__ void __launch_bounds__(256) fill_kernel(void* __restrict__ out, int64
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
     float x = value_at(key, sel_key, mix, (uint64_t)(pos_base + i), scale);
     if constexpr (DT == 0) {
-      ((float*)out)[i] = x;
-    } else if constexpr (DT == 1) {
-      ((__half*)out)[i] = __float2half_rn(x);
+      if constexpr (NT) __builtin_nontemporal_store(x, (float*)out + i);
+      else ((float*)out)[i] = x;
     } else {
-      __bf16 b = (__bf16)x;
-      ((uint16_t*)out)[i] = __builtin_bit_cast(uint16_t, b);
+      uint16_t h;
+      if constexpr (DT == 1) h = __builtin_bit_cast(uint16_t, __float2half_rn(x));
+      else h = __builtin_bit_cast(uint16_t, (__bf16)x);
+      if constexpr (NT) __builtin_nontemporal_store(h, (uint16_t*)out + i);
+      else ((uint16_t*)out)[i] = h;
     }
   }
 }
 
+template <bool NT>
+void launch_fill(int dt, int64_t blocks, hipStream_t st, void* out, int64_t n, uint64_t key, uint64_t sel_key,
+                 int mix, int64_t pos_base, float scale) {
+  if (dt == 0)
+    hipLaunchKernelGGL((fill_kernel<0, NT>), dim3((unsigned)blocks), dim3(256), 0, st, out, n, key, sel_key, mix, pos_base, scale);
+  else if (dt == 1)
+    hipLaunchKernelGGL((fill_kernel<1, NT>), dim3((unsigned)blocks), dim3(256), 0, st, out, n, key, sel_key, mix, pos_base, scale);
+  else
+    hipLaunchKernelGGL((fill_kernel<2, NT>), dim3((unsigned)blocks), dim3(256), 0, st, out, n, key, sel_key, mix, pos_base, scale);
+}
+
 }  // namespace
 
-// out: device buffer of n elements of dtype dt (0 f32, 1 f16, 2 bf16).
-// Returns 0 on success, a HIP error code otherwise.
+// out: device buffer of n elements of dtype dt (0 f32, 1 f16, 2 bf16); nt != 0
+// stores with non-temporal stores.  Returns 0 on success, a HIP error code
+// otherwise.
 extern "C" int synth_fill(void* out, int dt, int64_t n, uint64_t key, uint64_t sel_key, int mix,
-                          int64_t pos_base, float scale, void* stream) {
+                          int64_t pos_base, float scale, int nt, void* stream) {
   if (n <= 0) return 0;
   if (!out || dt < 0 || dt > 2) return (int)hipErrorInvalidValue;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   hipStream_t st = (hipStream_t)stream;
-  if (dt == 0)
-    hipLaunchKernelGGL(fill_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, st, out, n, key, sel_key, mix, pos_base, scale);
-  else if (dt == 1)
-    hipLaunchKernelGGL(fill_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, st, out, n, key, sel_key, mix, pos_base, scale);
-  else
-    hipLaunchKernelGGL(fill_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, st, out, n, key, sel_key, mix, pos_base, scale);
+  if (nt) launch_fill<true>(dt, blocks, st, out, n, key, sel_key, mix, pos_base, scale);
+  else launch_fill<false>(dt, blocks, st, out, n, key, sel_key, mix, pos_base, scale);
   return (int)hipGetLastError();
 }

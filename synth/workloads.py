@@ -162,20 +162,20 @@ class GpuRun:
     def _stream(self) -> int:
         return int(self.torch.cuda.current_stream(self.device).cuda_stream)
 
-    def _fill_rank_shard(self, buf, dt, rank, key, sigma, layer, mix=False, sel_key=0):
+    def _fill_rank_shard(self, buf, dt, rank, key, sigma, layer, mix=False, sel_key=0, nt=False):
         """Fill a shard-local buffer with the values at rank's positions; pads 0."""
         es = ESIZE[dt]
         base = buf.data_ptr()
         for (flat_off, numel, padded, sn, shard_off) in self.buckets:
             lo = flat_off + rank * sn
             self.SG.fill(base + shard_off * es, dt, sn, key, layer * self.P + lo, sigma,
-                         self._stream(), mix, sel_key)
+                         self._stream(), mix, sel_key, nt)
             pad_lo = max(lo, flat_off + numel)
             if pad_lo < lo + sn:
                 buf[shard_off + (pad_lo - lo): shard_off + sn].zero_()
 
-    def _fill_full(self, buf, dt, key, sigma, layer, mix=False, sel_key=0):
-        self.SG.fill(buf.data_ptr(), dt, self.P, key, layer * self.P, sigma, self._stream(), mix, sel_key)
+    def _fill_full(self, buf, dt, key, sigma, layer, mix=False, sel_key=0, nt=False):
+        self.SG.fill(buf.data_ptr(), dt, self.P, key, layer * self.P, sigma, self._stream(), mix, sel_key, nt)
         for (flat_off, numel, padded, sn, shard_off) in self.buckets:
             if padded > numel:
                 buf[flat_off + numel: flat_off + padded].zero_()
@@ -190,16 +190,18 @@ class GpuRun:
             for q in range(cfg.n_d):
                 self._fill_rank_shard(L["shards"][q], cfg.pdt, q, kw, cfg.sigma_w, layer)
 
-    def fill_grads(self, t: int, layer: int = 0):
+    def fill_grads(self, t: int, layer: int = 0, nt: bool = False):
+        """Step t's gradients of every rank (nt: written with non-temporal
+        stores, as a streaming receive would; the values are the same)."""
         cfg, L = self.cfg, self.layers[layer]
         for q in range(cfg.n_d):
             k = key_of(cfg.seed, STREAM_GRAD, q, t)
             ks = key_of(cfg.seed, STREAM_MIXSEL, q, t)
             if q in cfg.full_ranks:
-                self._fill_full(L["grads"][q], cfg.gdt, k, cfg.sigma_g, layer, cfg.mix, ks)
+                self._fill_full(L["grads"][q], cfg.gdt, k, cfg.sigma_g, layer, cfg.mix, ks, nt)
             else:
                 self._fill_rank_shard(L["grads"][q], cfg.gdt, cfg.owner, k, cfg.sigma_g, layer,
-                                      cfg.mix, ks)
+                                      cfg.mix, ks, nt)
 
     # -- the path -------------------------------------------------------------
     def step(self, t: int, layer: int = 0, stream=None, compute=None):

@@ -69,13 +69,16 @@ def test_streams_are_distinct():
 @pytest.mark.gpu
 @pytest.mark.parametrize("dt", [synth.F32, synth.F16, synth.BF16])
 @pytest.mark.parametrize("mix", [False, True])
-def test_gpu_fill_matches_host(gpu, dt, mix):
+@pytest.mark.parametrize("nt", [False, True])
+def test_gpu_fill_matches_host(gpu, dt, mix, nt):
+    """The GPU fill, with ordinary or non-temporal stores, equals the numpy
+    definition bit for bit."""
     import torch
     from synth import gpu as SG
     n, base = 3_000_001, 12_999_000_000
     k, ks = synth.key_of(5, synth.STREAM_GRAD, 3, 2), synth.key_of(5, synth.STREAM_MIXSEL, 3, 2)
     t = torch.empty(n, dtype=torch.float32 if dt == synth.F32 else torch.int16, device=gpu)
-    SG.fill(t.data_ptr(), dt, n, k, base, 1e-3, torch.cuda.current_stream().cuda_stream, mix, ks)
+    SG.fill(t.data_ptr(), dt, n, k, base, 1e-3, torch.cuda.current_stream().cuda_stream, mix, ks, nt)
     torch.cuda.synchronize()
     got = t.cpu().numpy().view(np.uint32 if dt == synth.F32 else np.uint16)
     pos = np.arange(base, base + n, dtype=np.int64)
