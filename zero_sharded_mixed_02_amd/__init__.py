@@ -147,7 +147,7 @@ def _tensor_props(x, name: str, esize: int):
         raise ValueError(f"{name}: elements of {x.element_size()} bytes ({x.dtype}), expected {esize}")
     if not x.is_contiguous():
         raise ValueError(f"{name} is not contiguous")
-    return int(x.numel()), x.device.type == "cuda"
+    return int(x.numel()), bool(x.is_cuda)
 
 
 def _arg(x, name: str, esize: int, need: int, exact: bool = False) -> int:
@@ -171,8 +171,22 @@ def _arg_list(xs, name: str, count: int, esize: int, need: int, exact: bool = Fa
     xs = list(xs)
     if len(xs) != count:
         raise ValueError(f"{name} has {len(xs)} entries, the plan needs {count}")
-    addrs = [_arg(x, f"{name}[{i}]", esize, need[i] if isinstance(need, (list, tuple)) else need, exact)
-             for i, x in enumerate(xs)]
+    per = isinstance(need, (list, tuple))
+    addrs = []
+    for i, x in enumerate(xs):
+        want = need[i] if per else need
+        # Fast path for the common case (a contiguous GPU tensor of the right
+        # element size and length); anything else goes through _arg, which
+        # raises with the argument's name.
+        try:
+            if x.element_size() == esize and x.is_contiguous() and x.is_cuda:
+                n = x.numel()
+                if n == want or (n > want and not exact):
+                    addrs.append(x.data_ptr())
+                    continue
+        except AttributeError:
+            pass
+        addrs.append(_arg(x, f"{name}[{i}]", esize, want, exact))
     return (ctypes.c_void_p * max(1, count))(*addrs)
 
 
