@@ -311,7 +311,10 @@ FILL_ORDER_PROBES = ("after_gradient_zero_then_nt_read_head", "after_gradient_ze
                      "after_gradient_zero_then_plain_read_32MB_head", "after_gradient_zero_then_plain_read_64MB_master",
                      "after_step_then_plain_read_64MB_master", "after_gradient_zero_then_plain_read_row_heads",
                      "after_step_then_plain_read_row_heads", "after_gradient_zero_then_plain_read_256MB_other",
-                     "after_gradient_nt_write", "after_gradient_nt_write_then_idle_5ms")
+                     "after_gradient_nt_write", "after_gradient_nt_write_then_idle_5ms",
+                     "after_gradient_zero_then_plain_read_64MB_master_as_int16",
+                     "after_gradient_zero_then_plain_read_64MB_other_as_f32",
+                     "after_gradient_zero_then_plain_read_32MB_other", "after_gradient_zero_then_plain_read_8MB_other")
 _PROBE_BYTES = 256 << 20
 
 
@@ -380,6 +383,18 @@ def _predecessor(torch, run, variant, spare, t):
     elif variant == "after_gradient_zero_then_plain_read_64MB_master":
         g.zero_()
         run.layers[0]["master"][: 16 << 20].sum()       # 64 MB of plain loads of the step's own state
+    elif variant == "after_gradient_zero_then_plain_read_64MB_master_as_int16":
+        g.zero_()
+        run.layers[0]["master"][: 16 << 20].view(torch.int16).sum()   # same bytes, the int16 sum kernel
+    elif variant == "after_gradient_zero_then_plain_read_64MB_other_as_f32":
+        g.zero_()
+        spare[: 32 << 20].view(torch.float32).sum()                  # same bytes, the float32 sum kernel
+    elif variant == "after_gradient_zero_then_plain_read_32MB_other":
+        g.zero_()
+        spare[: 16 << 20].sum()
+    elif variant == "after_gradient_zero_then_plain_read_8MB_other":
+        g.zero_()
+        spare[: 4 << 20].sum()
     elif variant == "after_step_then_plain_read_64MB_master":
         run.step(t)
         run.layers[0]["master"][: 16 << 20].sum()
