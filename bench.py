@@ -314,7 +314,8 @@ FILL_ORDER_PROBES = ("after_gradient_zero_then_nt_read_head", "after_gradient_ze
                      "after_gradient_nt_write", "after_gradient_nt_write_then_idle_5ms",
                      "after_gradient_zero_then_plain_read_64MB_master_as_int16",
                      "after_gradient_zero_then_plain_read_64MB_other_as_f32",
-                     "after_gradient_zero_then_plain_read_32MB_other", "after_gradient_zero_then_plain_read_8MB_other")
+                     "after_gradient_zero_then_plain_read_32MB_other", "after_gradient_zero_then_plain_read_8MB_other",
+                     "after_gradient_copy_in_runtime", "after_gradient_copy_in_library")
 _PROBE_BYTES = 256 << 20
 
 
@@ -395,6 +396,13 @@ def _predecessor(torch, run, variant, spare, t):
     elif variant == "after_gradient_zero_then_plain_read_8MB_other":
         g.zero_()
         spare[: 4 << 20].sum()
+    elif variant == "after_gradient_copy_in_runtime":
+        g.view(-1).copy_(spare)                         # 15 GB into the gradients by the runtime's copy kernel
+    elif variant == "after_gradient_copy_in_library":
+        import zero_sharded_mixed_02_amd as Z
+        if getattr(_predecessor, "copy_plan", None) is None or _predecessor.copy_plan[0] != g.numel():
+            _predecessor.copy_plan = (g.numel(), Z.zero_plan(g.numel(), 1, [g.numel()], 0, 1))
+        Z.zero_flatten(_predecessor.copy_plan[1], [spare], Z.ZERO_BF16, g.view(-1))   # the library's copy kernel
     elif variant == "after_step_then_plain_read_64MB_master":
         run.step(t)
         run.layers[0]["master"][: 16 << 20].sum()
