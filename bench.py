@@ -147,30 +147,32 @@ def _host_cpu():
     return {"cpu_model": model, "cpus_available": len(os.sched_getaffinity(0))}
 
 
-# GPU cycles of the spin queued before each timed call (about 2 ms): the host
-# marshals and launches the call while the GPU still spins, so the events
-# around the call bracket its kernels and not the host's argument checks
-# (which for the 193-tensor flatten take longer than its kernels).
-_SPIN_CYCLES = 5_000_000
+# GPU cycles of the spin queued before a block of timed calls (about 12 ms
+# at 2.4 GHz): the host enqueues the whole block while the GPU still spins,
+# so the calls then run back to back and the host's argument checks (which
+# for the 193-tensor flatten take longer than its kernels) do not count.
+_SPIN_CYCLES = 30_000_000
 
 
 def _time_launches(torch, fn, reps=20, warmup=3):
     """Average milliseconds per call of fn (one or more launches on torch's
-    current stream), from HIP events around each call, each call queued
-    behind a GPU spin so that host time does not count."""
+    current stream) over `reps` calls run back to back, from two HIP events
+    around the block.  The block is queued behind a GPU spin and one untimed
+    call (which takes any ramp-up after the spin), so neither host time nor
+    the idle spin counts."""
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    st = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    en = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    for i in range(reps):
-        torch.cuda._sleep(_SPIN_CYCLES)
-        st[i].record(stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(_SPIN_CYCLES)
+    fn()
+    e0.record(stream)
+    for _ in range(reps):
         fn()
-        en[i].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    return sum(s.elapsed_time(e) for s, e in zip(st, en)) / reps
+    return e0.elapsed_time(e1) / reps
 
 
 def _entry(ms, nbytes, elems):
