@@ -317,22 +317,27 @@ FILL_ORDER_PROBES = ("after_gradient_zero_then_nt_read_head", "after_gradient_ze
                      "after_gradient_zero_then_plain_read_64MB_master_as_int16",
                      "after_gradient_zero_then_plain_read_64MB_other_as_f32",
                      "after_gradient_zero_then_plain_read_32MB_other", "after_gradient_zero_then_plain_read_8MB_other",
-                     "after_gradient_copy_in_runtime", "after_gradient_copy_in_library")
+                     "after_gradient_copy_in_runtime", "after_gradient_copy_in_library",
+                     "after_gradient_zero_then_cached_probe_read_64MB_other",
+                     "after_gradient_zero_then_cached_probe_read_256MB_other",
+                     "after_zero_gradient_head_256MB", "after_zero_gradient_tail_256MB",
+                     "after_zero_gradient_row_heads_4MB", "after_zero_gradient_row_tails_4MB")
 _PROBE_BYTES = 256 << 20
 
 
-def _nt_read(torch, buf, byte_off):
-    """Non-temporal read of _PROBE_BYTES of buf from byte_off (the calibration
-    read probe)."""
+def _nt_read(torch, buf, byte_off, nbytes=None, cached=False):
+    """Read of nbytes (default _PROBE_BYTES) of buf from byte_off with the
+    calibration read probe: non-temporal loads, or cached loads."""
     from synth import gpu as SG
+    nread = _PROBE_BYTES if nbytes is None else nbytes
     sink = _nt_read.sink
     if sink is None:
         sink = _nt_read.sink = torch.empty(SG.probe_sink_words(_PROBE_BYTES), dtype=torch.int32, device="cuda")
     nbytes = buf.numel() * buf.element_size()
-    if byte_off < 0 or byte_off + _PROBE_BYTES > nbytes or byte_off % 16:
+    if byte_off < 0 or byte_off + nread > nbytes or byte_off % 16 or nread % 16 or nread > _PROBE_BYTES:
         raise ValueError("probe read outside the buffer")
-    SG.probe(SG.PROBE_READ, 0, buf.data_ptr() + byte_off, _PROBE_BYTES, sink.data_ptr(),
-             torch.cuda.current_stream().cuda_stream)
+    SG.probe(SG.PROBE_READ_CACHED if cached else SG.PROBE_READ, 0, buf.data_ptr() + byte_off, nread,
+             sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
 
 
 _nt_read.sink = None
@@ -398,6 +403,20 @@ def _predecessor(torch, run, variant, spare, t):
     elif variant == "after_gradient_zero_then_plain_read_8MB_other":
         g.zero_()
         spare[: 4 << 20].sum()
+    elif variant == "after_gradient_zero_then_cached_probe_read_64MB_other":
+        g.zero_()
+        _nt_read(torch, spare, 0, 64 << 20, cached=True)   # 64 MB of cached loads in ~10 us
+    elif variant == "after_gradient_zero_then_cached_probe_read_256MB_other":
+        g.zero_()
+        _nt_read(torch, spare, 0, 256 << 20, cached=True)
+    elif variant == "after_zero_gradient_head_256MB":
+        g.view(-1)[: 128 << 20].zero_()                 # cached stores to 256 MB only: the rows' start
+    elif variant == "after_zero_gradient_tail_256MB":
+        g.view(-1)[-(128 << 20):].zero_()               # ... the rows' end
+    elif variant == "after_zero_gradient_row_heads_4MB":
+        g[:, : 2 << 20].zero_()                         # ... the first 4 MB of every row
+    elif variant == "after_zero_gradient_row_tails_4MB":
+        g[:, -(2 << 20):].zero_()                       # ... the last 4 MB of every row
     elif variant == "after_gradient_copy_in_runtime":
         g.view(-1).copy_(spare)                         # 15 GB into the gradients by the runtime's copy kernel
     elif variant == "after_gradient_copy_in_library":

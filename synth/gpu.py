@@ -51,7 +51,7 @@ def fill(addr: int, dt: int, n: int, key: int, pos_base: int, sigma: float, stre
         raise RuntimeError(f"synth_fill failed with HIP error {err}")
 
 
-PROBE_READ, PROBE_WRITE, PROBE_COPY = 0, 1, 2
+PROBE_READ, PROBE_WRITE, PROBE_COPY, PROBE_READ_CACHED = 0, 1, 2, 3
 
 
 def probe_sink_words(nbytes: int) -> int:
@@ -60,8 +60,9 @@ def probe_sink_words(nbytes: int) -> int:
 
 
 def probe(kind: int, dst: int, src: int, nbytes: int, sink: int, stream: int) -> None:
-    """One calibration launch: read nbytes at src, write nbytes at dst, or
-    copy nbytes from src to dst (16-byte aligned, nbytes a multiple of 16)."""
+    """One calibration launch: read nbytes at src (non-temporal loads, or
+    cached loads with PROBE_READ_CACHED), write nbytes at dst, or copy nbytes
+    from src to dst (16-byte aligned, nbytes a multiple of 16)."""
     err = load().synth_probe(kind, ctypes.c_void_p(dst), ctypes.c_void_p(src), nbytes, ctypes.c_void_p(sink),
                              ctypes.c_void_p(stream))
     if err != 0:

@@ -28,9 +28,16 @@ __device__ __forceinline__ uint32_t wave_lane(int units_per_lane) {
   return (threadIdx.x >> 6) * (64 * units_per_lane) + (threadIdx.x & 63);
 }
 
-// Reads `units` 16-byte units; each workgroup stores one word (the xor of
-// what its first lane read), so the loads cannot be dropped.
-template <int T, int U>
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const gu32x4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+// Reads `units` 16-byte units (NT: non-temporal loads; else ordinary cached
+// loads); each workgroup stores one word (the xor of what its first lane
+// read), so the loads cannot be dropped.
+template <int T, int U, bool NT>
 __global__ void __launch_bounds__(T) probe_read(const u32x4* src, int64_t units, uint32_t* sink) {
   const int64_t first = (int64_t)blockIdx.x * T * U;
   u32x4 acc = {0u, 0u, 0u, 0u};
@@ -38,13 +45,13 @@ __global__ void __launch_bounds__(T) probe_read(const u32x4* src, int64_t units,
     const gu32x4* wv = (const gu32x4*)(src + first) + wave_lane(U);
     u32x4 r[U];
 #pragma unroll
-    for (int i = 0; i < U; ++i) r[i] = __builtin_nontemporal_load(wv + i * 64);
+    for (int i = 0; i < U; ++i) r[i] = load16<NT>(wv + i * 64);
 #pragma unroll
     for (int i = 0; i < U; ++i) acc ^= r[i];
   } else {
     for (int i = 0; i < U; ++i) {
       const int64_t u = first + threadIdx.x + (int64_t)i * T;
-      if (u < units) acc ^= __builtin_nontemporal_load((const gu32x4*)(src + u));
+      if (u < units) acc ^= load16<NT>((const gu32x4*)(src + u));
     }
   }
   const uint32_t x = __builtin_amdgcn_readfirstlane(acc.x ^ acc.y ^ acc.z ^ acc.w);
@@ -93,7 +100,7 @@ int64_t blocks_for(int64_t units, int per_block) { return (units + per_block - 1
 
 // kind 0: read `bytes` at src (sink: one word per workgroup, see
 // synth_probe_sink_words); 1: write `bytes` at dst; 2: copy `bytes` from src
-// to dst.  bytes must be a multiple of 16 and pointers 16-byte aligned.
+// to dst; 3: as 0 with ordinary cached loads instead of non-temporal ones.  bytes must be a multiple of 16 and pointers 16-byte aligned.
 // Returns 0 or a HIP error code.
 extern "C" int64_t synth_probe_sink_words(int64_t bytes) { return blocks_for(bytes / 16, kReadThreads * kReadUnits); }
 
@@ -102,11 +109,15 @@ extern "C" int synth_probe(int kind, void* dst, const void* src, int64_t bytes, 
   if ((bytes & 15) || ((uintptr_t)dst & 15) || ((uintptr_t)src & 15)) return (int)hipErrorInvalidValue;
   const int64_t units = bytes / 16;
   hipStream_t st = (hipStream_t)stream;
-  if (kind == 0) {
+  if (kind == 0 || kind == 3) {
     const int64_t blocks = blocks_for(units, kReadThreads * kReadUnits);
     if (!src || !sink || blocks > INT32_MAX) return (int)hipErrorInvalidValue;
-    hipLaunchKernelGGL((probe_read<kReadThreads, kReadUnits>), dim3((unsigned)blocks), dim3(kReadThreads), 0, st,
-                       (const u32x4*)src, units, sink);
+    if (kind == 0)
+      hipLaunchKernelGGL((probe_read<kReadThreads, kReadUnits, true>), dim3((unsigned)blocks), dim3(kReadThreads), 0,
+                         st, (const u32x4*)src, units, sink);
+    else
+      hipLaunchKernelGGL((probe_read<kReadThreads, kReadUnits, false>), dim3((unsigned)blocks), dim3(kReadThreads), 0,
+                         st, (const u32x4*)src, units, sink);
   } else if (kind == 1) {
     const int64_t blocks = blocks_for(units, kWriteThreads * kWriteUnits);
     if (!dst || blocks > INT32_MAX) return (int)hipErrorInvalidValue;
