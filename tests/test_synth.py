@@ -116,3 +116,42 @@ def test_balanced_cus(k):
         assert np.bincount([i % dies for i in cus], minlength=dies).tolist() == [want] * dies
     with pytest.raises(ValueError):
         balanced_cus(12, n, dies)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("nbytes", [1 << 20, (1 << 20) + 16 * 777])
+def test_calibration_probes(gpu, nbytes):
+    """The HBM calibration probes do what they claim, also when the last
+    workgroup is partial: the copy copies every byte, the write writes its
+    pattern everywhere and nothing past the end, and both reads (non-temporal
+    and cached) see the data (each workgroup's sink word is the xor of the
+    16-byte units its first lane read)."""
+    import torch
+    from synth import gpu as SG
+    n = nbytes // 4
+    stream = torch.cuda.current_stream().cuda_stream
+    src = torch.randint(-2**31, 2**31 - 1, (n + 64,), dtype=torch.int32, device=gpu)
+    dst = torch.zeros(n + 64, dtype=torch.int32, device=gpu)
+    SG.probe(SG.PROBE_COPY, dst.data_ptr(), src.data_ptr(), nbytes, 0, stream)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:n], src[:n]) and not torch.any(dst[n:])
+    SG.probe(SG.PROBE_WRITE, dst.data_ptr(), 0, nbytes, 0, stream)
+    torch.cuda.synchronize()
+    assert torch.all(dst[:n] == 0x3c003c00) and not torch.any(dst[n:])
+    host = src[:n].cpu().numpy().view(np.uint32).reshape(-1, 4)   # 16-byte units
+    words = SG.probe_sink_words(nbytes)
+    for kind in (SG.PROBE_READ, SG.PROBE_READ_CACHED):
+        sink = torch.zeros(words, dtype=torch.int32, device=gpu)
+        SG.probe(kind, 0, src.data_ptr(), nbytes, sink.data_ptr(), stream)
+        torch.cuda.synchronize()
+        got = sink.cpu().numpy().view(np.uint32)
+        # Workgroup b's first lane (lane 0 of wave 0) reads units b*T*U + i*64 (i < U) on the
+        # full-block path, units b*T*U + i*T on the last block's checked path.
+        T, U = 1024, 8
+        units = host.shape[0]
+        for b in range(words):
+            first = b * T * U
+            idx = [first + i * 64 for i in range(U)] if first + T * U <= units else \
+                  [first + i * T for i in range(U) if first + i * T < units]
+            want = np.bitwise_xor.reduce(np.bitwise_xor.reduce(host[idx], axis=0)) if idx else 0
+            assert got[b] == want, (kind, b)
