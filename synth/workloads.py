@@ -25,7 +25,7 @@ Workload shapes (stand-ins for the models on the ZeRO pages), by name:
 from __future__ import annotations
 
 from dataclasses import dataclass, replace
-from typing import List, Sequence
+from typing import List
 
 import numpy as np
 
