@@ -968,6 +968,9 @@ def main():
     ap.add_argument("--owner", type=int, default=None, help="owning rank (default: the workload's)")
     ap.add_argument("--shard-align", type=int, default=None, help="shard alignment in elements")
     ap.add_argument("--bucket-cap", type=int, default=None, help="bucket cap in elements (0 = one bucket)")
+    ap.add_argument("--window", nargs=2, type=int, metavar=("PERIOD", "OPEN"), default=None,
+                    help="write window of the timed step in counter ticks (0 0 = none); default: the library's "
+                         "automatic choice")
     ap.add_argument("--headline-only", action="store_true",
                     help="time the fused step only (no kernels, calibration or CPU baseline objects)")
     ap.add_argument("--fill-order", action="store_true",
@@ -1038,6 +1041,9 @@ def main():
     if cfg.stage == 3:
         raise SystemExit("bench.py times the Stage-1/2 fused step; the Stage-3 workload is a parity case")
     torch.cuda.init()
+    if args.window is not None:
+        import zero_sharded_mixed_02_amd as Z
+        Z.zero_set_write_window(*args.window)
     log(f"setting up {cfg.name}: psi={cfg.psi} n_d={cfg.n_d}")
     run = GpuRun(cfg)
     S = run.S
@@ -1121,7 +1127,8 @@ def main():
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": launch_bytes,
                      "avg_launch_ms": avg_launch_s * 1e3, "kernel": "step_vec_kernel (fused)"},
-        "write_window": "automatic (library default)",
+        "write_window": "automatic (library default)" if args.window is None else
+                        {"period_ticks": args.window[0], "open_ticks": args.window[1]},
         # Sustained runs: the mean launch time of each block of 100 timed steps.
         "per_100_steps_ms": [sum(launch_ms[i:i + 100]) / 100 for i in range(0, len(launch_ms) - 99, 100)]
         if len(launch_ms) >= 200 else None,
@@ -1140,6 +1147,9 @@ def main():
     del run
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+    if args.window is not None:   # the other measurements use the library's automatic choice
+        import zero_sharded_mixed_02_amd as Z
+        Z.zero_set_write_window(-1)
     if not args.headline_only:
         out["kernels"] = measure_kernels_compact(torch)
         out["calibration"] = measure_calibration(torch)

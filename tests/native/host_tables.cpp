@@ -480,9 +480,9 @@ int main() {
                           (float*)(uintptr_t)fake_base(2), (float*)(uintptr_t)fake_base(3),
                           (void*)(uintptr_t)fake_base(4), ZERO_F16, 1, nullptr) == ZERO_OK,
            "large step failed: %s", zero_last_error());
-    // 1024 resident workgroups x 4096 elements x 154 bytes at 6.5 TB/s, halved,
-    // in 10 ns ticks: 4968; open for the written 14/154 of it: 451.
-    EXPECT(g_steps.size() == 1 && g_steps[0].a.win_period == 4968 && g_steps[0].a.win_open == 451,
+    // 1024 resident workgroups x 4096 elements x 154 bytes at 6.5 TB/s, times
+    // 0.62, in 10 ns ticks: 6161; open for the written 14/154 of it: 560.
+    EXPECT(g_steps.size() == 1 && g_steps[0].a.win_period == 6161 && g_steps[0].a.win_open == 560,
            "automatic window of a large fused launch: (%u, %u)", g_steps.empty() ? 0u : g_steps[0].a.win_period,
            g_steps.empty() ? 0u : g_steps[0].a.win_open);
     EXPECT(zero_adam_step(p, 3, &hp, 1, nullptr, (const float*)(uintptr_t)fake_base(5),
@@ -490,15 +490,15 @@ int main() {
                           (float*)(uintptr_t)fake_base(3), (void*)(uintptr_t)fake_base(4), ZERO_F16, 1,
                           nullptr) == ZERO_OK, "large from-reduced step failed: %s", zero_last_error());
     EXPECT(g_steps.size() == 2 && g_steps[1].a.win_period == 0, "window on Adam from the reduced gradient");
-    // The reduction: 768 resident x 4096 x 132 bytes -> 3194 ticks, open 1/16.
+    // The reduction: 768 resident x 4096 x 132 bytes -> 3960 ticks, open 1/16.
     zero_grad_src src16 = {ZERO_BF16, 64, ptrs.data(), nullptr};
     EXPECT(zero_shard_reduce(p, 3, &src16, 1.0 / 64, (float*)(uintptr_t)fake_base(5), nullptr) == ZERO_OK,
            "large reduce failed: %s", zero_last_error());
-    EXPECT(g_steps.size() == 3 && g_steps[2].a.win_period == 3194 && g_steps[2].a.win_open == 199,
+    EXPECT(g_steps.size() == 3 && g_steps[2].a.win_period == 3960 && g_steps[2].a.win_open == 247,
            "automatic window of a large reduce launch: (%u, %u)", g_steps.size() < 3 ? 0u : g_steps[2].a.win_period,
            g_steps.size() < 3 ? 0u : g_steps[2].a.win_open);
     // Three generations of resident workgroups (3 x 1024 x 4096 elements):
-    // half the period, 2484 ticks, open 225.
+    // half the period, 3080 ticks, open 280.
     {
       std::vector<int64_t> s3 = {(int64_t)3 * 1024 * 4096 * 64};
       zero_plan_t p3;
@@ -508,7 +508,7 @@ int main() {
                             (float*)(uintptr_t)fake_base(2), (float*)(uintptr_t)fake_base(3),
                             (void*)(uintptr_t)fake_base(4), ZERO_F16, 1, nullptr) == ZERO_OK,
              "3-generation step failed: %s", zero_last_error());
-      EXPECT(g_steps.size() == 1 && g_steps[0].a.win_period == 2484 && g_steps[0].a.win_open == 225,
+      EXPECT(g_steps.size() == 1 && g_steps[0].a.win_period == 3080 && g_steps[0].a.win_open == 280,
              "automatic window of a 3-generation launch: (%u, %u)", g_steps.empty() ? 0u : g_steps[0].a.win_period,
              g_steps.empty() ? 0u : g_steps[0].a.win_open);
       zero_plan_destroy(p3);
@@ -566,11 +566,11 @@ int main() {
     EXPECT(zero_set_write_window(-1, 0) == ZERO_OK, "automatic default refused");
     EXPECT(window_on(sa) == automatic && window_on(nullptr) == automatic, "not back to automatic");
     // The automatic period follows the counter rate the device reports: the
-    // same launch at 50, 100 and 200 MHz takes 2484, 4968 and 9937 ticks
-    // (1024 resident x 4096 elements x 154 B at 6.5 TB/s, halved); no rate,
+    // same launch at 50, 100 and 200 MHz takes 3080, 6161 and 12322 ticks
+    // (1024 resident x 4096 elements x 154 B at 6.5 TB/s, times 0.62); no rate,
     // no window.
     const double rates[3] = {5e7, 1e8, 2e8};
-    const uint32_t want_p[3] = {2484, 4968, 9937}, want_o[3] = {225, 451, 903};
+    const uint32_t want_p[3] = {3080, 6161, 12322}, want_o[3] = {280, 560, 1120};
     for (int i = 0; i < 3; ++i) {
       zk::g_wall_clock_hz = rates[i];
       EXPECT(window_on(sb) == std::make_pair(want_p[i], want_o[i]), "automatic window at %.0f Hz: (%u, %u)",

@@ -171,7 +171,7 @@ bool encode_window(int64_t period_ticks, int64_t open_ticks, uint64_t& w) {
 // well below the lifetime of a workgroup, or every generation of resident
 // workgroups ends up taking a whole number of periods.  Sweeps on MI355X of
 // the fused step (7.5B at N_d = 64, 13B at N_d = 16, a Stage-3 layer) and of
-// the reduction found the best period near half the time one generation of
+// the reduction found the best period near 0.62 of the time one generation of
 // resident workgroups takes to stream its bytes at ~6.5 TB/s, and the best
 // opening near the written share of the bytes (at least 1/16 of the period).
 // Launches with few ranks per written element or few elements gain nothing.
@@ -185,6 +185,7 @@ constexpr int kAutoMinRanks = 16;
 constexpr double kAutoFullGenerations = 6.0;
 constexpr int64_t kAutoMinElems = int64_t(1) << 23;
 constexpr double kAutoStreamShare = 6.5e12 / 8.192e12;   // 6.5 TB/s on MI355X
+constexpr double kAutoPeriodShare = 0.62;                 // of one generation's streaming time
 
 void auto_window(int mode, int gdt, int pdt, int ndc, int n_ranks, int64_t elems, int64_t blocks,
                  zk::StepArgs& a) {
@@ -197,7 +198,7 @@ void auto_window(int mode, int gdt, int pdt, int ndc, int n_ranks, int64_t elems
   const double read = 2.0 * n_ranks + (mode == zk::kFused ? 12.0 : (a.flags & zk::kFlagInitFromOut) ? 4.0 : 0.0);
   const double written = mode == zk::kFused ? 14.0 : 4.0;
   const double gen_bytes = (double)resident * zk::kStepThreads * zk::kStepVec * (read + written);
-  double period = gen_bytes / (kAutoStreamShare * peak) / 2.0 * hz;
+  double period = gen_bytes / (kAutoStreamShare * peak) * kAutoPeriodShare * hz;
   period *= std::min(1.0, (double)blocks / resident / kAutoFullGenerations);
   const double min_period = 2e-6 * hz;   // 2 us
   period = std::min<double>(std::max(period, min_period), (double)zk::kMaxWindowPeriod);
