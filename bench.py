@@ -740,9 +740,11 @@ def measure_windows(torch):
     return out
 
 
-def _stage3_with_compute(torch, run, t, nl, P, S, tokens=2048, splits=()):
-    import zero_sharded_mixed_02_amd as Z
-    h = 8192
+def stage3_gemm_compute(torch, run, tokens=2048, h=8192):
+    """The Stage-3 layer-compute stand-in: compute(layer, buf) runs the six
+    weight GEMMs of a transformer layer's forward (q, k, v, output, MLP in and
+    out) on `tokens` tokens in fp16, reading the weights from the gathered
+    layer buffer `buf` at the plan's tensor offsets."""
     offs = [run.plan.tensor(i)[1] for i in range(len(run.cfg.sizes))]
     x = (torch.randn(tokens, h, device="cuda") * 0.5).to(torch.float16)
 
@@ -756,6 +758,17 @@ def _stage3_with_compute(torch, run, t, nl, P, S, tokens=2048, splits=()):
         q @ w(buf, 8, h, h)
         hid = x @ w(buf, 12, h, 4 * h)
         hid @ w(buf, 14, 4 * h, h)
+    return compute
+
+
+def _stage3_with_compute(torch, run, t, nl, P, S, tokens=2048, splits=()):
+    import zero_sharded_mixed_02_amd as Z
+    h = 8192
+    compute = stage3_gemm_compute(torch, run, tokens, h)
+    # The compute reads real weights: GEMMs over the zero-filled buffer run
+    # about 30% faster on MI355X (MFMA power, and so the clock, depends on the
+    # data).
+    Z.zero_gather_pack(run.plan, list(run.layers[0]["shards"]), run.cfg.pdt, run.full)
 
     def compute_only():
         for layer in range(nl):
@@ -833,10 +846,125 @@ def measure_stage3_overlap(torch, splits=(16, 32, 64)):
     t = [1]
     res = _stage3_with_compute(torch, run, t, run.cfg.layers, run.P, run.S, splits=splits)
     res["temp_buffer_bytes"] = {"serial": 2 * run.P, "pipelined": 4 * run.P}
+    res["elastic_compute"] = _stage3_elastic(torch, run, t, res["gather_only_ms"] / run.cfg.layers)
+    res["contention"] = _stage3_contention(torch, run, stage3_gemm_compute(torch, run))
     del run
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
+
+
+def _stage3_elastic(torch, run, t, gather_layer_ms, lds_sizes=(4, 32768, 65536), ratios=(1.0, 4.0),
+                    blocks_per_cu=64):
+    """The Stage-3 loop with an elastic compute stand-in in place of the
+    GEMMs: many short workgroups of dependent FMAs over the gathered weights
+    (synth elastic_compute), whose retiring workgroups leave CUs that a kernel
+    on another stream can take.  Per LDS size per workgroup (which bounds the
+    workgroups a CU holds, and so the wave slots left to the gathers) and per
+    ratio of compute to one layer's gather (set from a timed calibration
+    launch): the compute alone, the serial loop, the prefetching loop and the
+    share of the gathers the prefetch hides."""
+    from synth import gpu as SG
+    nl = run.cfg.layers
+    blocks = blocks_per_cu * SG.cu_count()
+    sink = torch.empty(blocks, dtype=torch.float32, device="cuda")
+
+    def compute_of(iters, lds):
+        def compute(layer, buf):
+            SG.elastic_compute(buf.data_ptr(), buf.numel(), iters, blocks, sink.data_ptr(),
+                               torch.cuda.current_stream().cuda_stream, lds)
+        return compute
+
+    out = {"workgroups": blocks, "threads_per_workgroup": 256, "gather_per_layer_ms": gather_layer_ms}
+    probe_iters = 4096
+    for lds in lds_sizes:
+        probe_ms = _time_launches(torch, lambda: compute_of(probe_iters, lds)(0, run.full), reps=10, warmup=2)
+        o = out[f"lds_{lds}"] = {"calibration": {"iters": probe_iters, "ms": probe_ms}}
+        for ratio in ratios:
+            iters = max(1, round(probe_iters * ratio * gather_layer_ms / probe_ms))
+            compute = compute_of(iters, lds)
+
+            def compute_only(compute=compute):
+                for layer in range(nl):
+                    compute(layer, run.full)
+            e = {"iters": iters, "compute_only_ms": _time_launches(torch, compute_only, reps=5, warmup=2)}
+            for name, pipelined in (("serial", False), ("pipelined", True)):
+                def loop(pipelined=pipelined, compute=compute):
+                    t[0] += 1
+                    run.layer_loop(t[0], pipelined, compute)
+                e[name + "_ms"] = _time_launches(torch, loop, reps=5, warmup=2)
+            e["gather_hidden_fraction"] = (e["serial_ms"] - e["pipelined_ms"]) / (nl * gather_layer_ms)
+            o[f"compute_{ratio:g}x_gather"] = e
+            log(f"stage3 elastic compute, LDS {lds} B, {ratio:g}x gather: " + ", ".join(
+                f"{a} {b:.3f}" if isinstance(b, float) else f"{a} {b}" for a, b in e.items()))
+    del sink
+    return out
+
+
+def _span_ms(torch, fn, reps=5, warm=4):
+    """Average milliseconds from before to after fn (which may fork work onto
+    other streams and must join them back), each rep timed after `warm`
+    untimed calls queued back to back.  No spin first: GEMM-heavy work runs
+    at boost for a few ms after an idle spell and then dips below its steady
+    rate (one layer of the Stage-3 stand-in: ~2.7 ms, then ~3.4, then 2.56),
+    so the timed call has to come after the dip."""
+    main = torch.cuda.current_stream()
+    tot = 0.0
+    for _ in range(reps):
+        for _ in range(warm):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main)
+        fn()
+        e1.record(main)
+        torch.cuda.synchronize()
+        tot += e0.elapsed_time(e1)
+    return tot / reps
+
+
+def _pair(torch, side, first, second):
+    """fn launching `first` on the side stream and, after a ~10 us spin on the
+    current stream, `second` there, so `first` reaches the CUs first."""
+    def fn():
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            first()
+        torch.cuda._sleep(20_000)
+        second()
+        main.wait_stream(side)
+    return fn
+
+
+def _stage3_contention(torch, run, compute, caps=(4096, 512, 128, 32, 8)):
+    """One layer's GEMM compute stand-in beside one layer's worth of data
+    movement on a second stream, each order: gather_pack (full grid), and a
+    copy of the same bytes on a grid capped at a given number of workgroups.
+    Per companion the span alone, with the compute launched first, and with
+    the companion first, against the compute alone."""
+    import zero_sharded_mixed_02_amd as Z
+    from synth import gpu as SG
+    side = torch.cuda.Stream()
+    gdst = torch.empty_like(run.full)
+    a, b = torch.full_like(run.full, 7), torch.empty_like(run.full)
+    nbytes = 2 * run.P // 16 * 16
+    shards = list(run.layers[0]["shards"])
+
+    def layer():
+        compute(0, run.full)
+    comps = {"gather_pack": lambda: Z.zero_gather_pack(run.plan, shards, run.cfg.pdt, gdst)}
+    for cap in caps:
+        comps[f"copy_{cap}_workgroups"] = lambda cap=cap: SG.probe_copy_capped(
+            b.data_ptr(), a.data_ptr(), nbytes, cap, torch.cuda.current_stream().cuda_stream)
+    out = {"compute_ms": _span_ms(torch, layer), "bytes_each_way": nbytes}
+    for name, c in comps.items():
+        e = {"alone_ms": _span_ms(torch, c), "compute_first_ms": _span_ms(torch, _pair(torch, side, layer, c)),
+             "companion_first_ms": _span_ms(torch, _pair(torch, side, c, layer))}
+        e["best_saving_ms"] = out["compute_ms"] + e["alone_ms"] - min(e["compute_first_ms"], e["companion_first_ms"])
+        out[name] = e
+        log(f"stage3 contention {name}: " + ", ".join(f"{k} {v:.3f}" for k, v in e.items()))
+    del gdst, a, b
+    return out
 
 
 def _counter_means(path, kernel_substr, counter):
@@ -921,6 +1049,12 @@ def counter_run(torch):
     sizes["P_stage3"] = run.P
     for _ in range(2):
         Z.zero_gather_pack(run.plan, list(run.layers[0]["shards"]), run.cfg.pdt, run.full)
+        torch.cuda.synchronize()
+    # The Stage-3 layer-compute stand-in's GEMMs over the gathered layer,
+    # for their cache and fabric counters.
+    compute = stage3_gemm_compute(torch, run)
+    for _ in range(2):
+        compute(0, run.full)
         torch.cuda.synchronize()
     print(json.dumps({"counter_run": sizes}))
 

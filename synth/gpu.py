@@ -24,11 +24,17 @@ def load():
                                   ctypes.c_void_p, ctypes.c_void_p]
         L.synth_probe_sink_words.restype = ctypes.c_int64
         L.synth_probe_sink_words.argtypes = [ctypes.c_int64]
+        L.synth_probe_copy_capped.restype = ctypes.c_int
+        L.synth_probe_copy_capped.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                              ctypes.c_void_p]
         L.synth_cu_count.restype = ctypes.c_int
         L.synth_cu_count.argtypes = [ctypes.POINTER(ctypes.c_int)]
         L.synth_stream_create_cu_masked.restype = ctypes.c_int
         L.synth_stream_create_cu_masked.argtypes = [ctypes.c_uint32, ctypes.POINTER(ctypes.c_uint32),
                                                     ctypes.POINTER(ctypes.c_void_p)]
+        L.synth_elastic_compute.restype = ctypes.c_int
+        L.synth_elastic_compute.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
         L.synth_stream_destroy.restype = ctypes.c_int
         L.synth_stream_destroy.argtypes = [ctypes.c_void_p]
         L.synth_fill.restype = ctypes.c_int
@@ -67,6 +73,15 @@ def probe(kind: int, dst: int, src: int, nbytes: int, sink: int, stream: int) ->
                              ctypes.c_void_p(stream))
     if err != 0:
         raise RuntimeError(f"synth_probe({kind}) failed with HIP error {err}")
+
+
+def probe_copy_capped(dst: int, src: int, nbytes: int, max_blocks: int, stream: int) -> None:
+    """The copy probe on a grid of at most max_blocks workgroups, each walking
+    the buffer in strides of the grid (a rate-limited background copy)."""
+    err = load().synth_probe_copy_capped(ctypes.c_void_p(dst), ctypes.c_void_p(src), nbytes, max_blocks,
+                                         ctypes.c_void_p(stream))
+    if err != 0:
+        raise RuntimeError(f"synth_probe_copy_capped failed with HIP error {err}")
 
 
 def cu_count() -> int:
@@ -124,3 +139,15 @@ class MaskedStream:
             self.torch.synchronize()
             load().synth_stream_destroy(ctypes.c_void_p(self.handle))
             self.handle = None
+
+
+def elastic_compute(w_addr: int, n: int, iters: int, blocks: int, out_addr: int, stream: int,
+                    lds_bytes: int = 4) -> None:
+    """The elastic compute stand-in of the Stage-3 prefetch study (see
+    streams.hip): `blocks` workgroups, each thread `iters` dependent FMAs on a
+    16-bit weight of the n at w_addr, each workgroup holding lds_bytes of LDS;
+    one float per workgroup to out_addr."""
+    err = load().synth_elastic_compute(ctypes.c_void_p(w_addr), n, iters, blocks, lds_bytes,
+                                       ctypes.c_void_p(out_addr), ctypes.c_void_p(stream))
+    if err != 0:
+        raise RuntimeError(f"synth_elastic_compute failed with HIP error {err}")

@@ -94,6 +94,30 @@ __global__ void __launch_bounds__(T) probe_copy(u32x4* dst, const u32x4* src, in
   }
 }
 
+// A copy on a capped grid: each workgroup walks chunks of T * U units
+// blockIdx.x, blockIdx.x + gridDim.x, ... (full chunks, wave layout as above);
+// workgroup 0 then copies the ragged tail unit by unit.  With few workgroups
+// it holds a few CUs and draws a fraction of HBM bandwidth, as a rate-limited
+// background transfer would.
+template <int T, int U>
+__global__ void __launch_bounds__(T) probe_copy_capped(u32x4* dst, const u32x4* src, int64_t units) {
+  const int64_t chunk = (int64_t)T * U;
+  const int64_t full = units / chunk;
+  const uint32_t wl = wave_lane(U);
+  for (int64_t c = blockIdx.x; c < full; c += gridDim.x) {
+    const gu32x4* sw = (const gu32x4*)(src + c * chunk) + wl;
+    gu32x4* dw = (gu32x4*)(dst + c * chunk) + wl;
+    u32x4 r[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) r[i] = __builtin_nontemporal_load(sw + i * 64);
+#pragma unroll
+    for (int i = 0; i < U; ++i) __builtin_nontemporal_store(r[i], dw + i * 64);
+  }
+  if (blockIdx.x == 0)
+    for (int64_t u = full * chunk + threadIdx.x; u < units; u += T)
+      __builtin_nontemporal_store(__builtin_nontemporal_load((const gu32x4*)(src + u)), (gu32x4*)(dst + u));
+}
+
 int64_t blocks_for(int64_t units, int per_block) { return (units + per_block - 1) / per_block; }
 
 }  // namespace
@@ -131,5 +155,21 @@ extern "C" int synth_probe(int kind, void* dst, const void* src, int64_t bytes, 
   } else {
     return (int)hipErrorInvalidValue;
   }
+  return (int)hipGetLastError();
+}
+
+// Copy `bytes` from src to dst on at most `max_blocks` workgroups of the copy
+// shape (fewer when the copy has fewer chunks).  Same alignment rules as
+// synth_probe.  Returns 0 or a HIP error code.
+extern "C" int synth_probe_copy_capped(void* dst, const void* src, int64_t bytes, int32_t max_blocks, void* stream) {
+  if (bytes <= 0) return 0;
+  if (!dst || !src || max_blocks <= 0 || (bytes & 15) || ((uintptr_t)dst & 15) || ((uintptr_t)src & 15))
+    return (int)hipErrorInvalidValue;
+  const int64_t units = bytes / 16;
+  int64_t blocks = units / (kCopyThreads * kCopyUnits);
+  if (blocks > max_blocks) blocks = max_blocks;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL((probe_copy_capped<kCopyThreads, kCopyUnits>), dim3((unsigned)blocks), dim3(kCopyThreads), 0,
+                     (hipStream_t)stream, (u32x4*)dst, (const u32x4*)src, units);
   return (int)hipGetLastError();
 }

@@ -155,3 +155,45 @@ def test_calibration_probes(gpu, nbytes):
                   [first + i * T for i in range(U) if first + i * T < units]
             want = np.bitwise_xor.reduce(np.bitwise_xor.reduce(host[idx], axis=0)) if idx else 0
             assert got[b] == want, (kind, b)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("lds", [4, 32768])
+def test_elastic_compute(gpu, lds):
+    """The Stage-3 study's elastic compute stand-in computes what it says:
+    per thread the affine recurrence x <- a x + b from its weight, which has
+    the closed form a^k x0 + b (1 - a^k) / (1 - a), summed per workgroup;
+    and it rejects an LDS size outside [4, 64 KiB]."""
+    import torch
+    from synth import gpu as SG
+    n, blocks, iters = 700, 5, 300
+    w = torch.randint(0, 65536, (n,), dtype=torch.int32).to(torch.int16).to(gpu)
+    out = torch.zeros(blocks, dtype=torch.float32, device=gpu)
+    stream = torch.cuda.current_stream().cuda_stream
+    SG.elastic_compute(w.data_ptr(), n, iters, blocks, out.data_ptr(), stream, lds)
+    torch.cuda.synchronize()
+    a, b = np.float64(np.float32(0.999)), np.float64(np.float32(1e-3))
+    x0 = w.cpu().numpy().view(np.uint16).astype(np.float64) * 2.0 ** -16
+    idx = np.arange(blocks * 256) % n
+    x = a ** iters * x0[idx] + b * (1 - a ** iters) / (1 - a)
+    want = x.reshape(blocks, 256).sum(axis=1)
+    np.testing.assert_allclose(out.cpu().numpy(), want, rtol=1e-4)
+    for bad in (0, 65540):
+        with pytest.raises(RuntimeError):
+            SG.elastic_compute(w.data_ptr(), n, iters, blocks, out.data_ptr(), stream, bad)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("nbytes", [16 * 1023, 16 * (1024 * 37 + 5), 1 << 22])
+@pytest.mark.parametrize("cap", [1, 3, 256])
+def test_capped_copy_probe(gpu, nbytes, cap):
+    """The capped-grid copy copies every byte and nothing past the end, with
+    a ragged tail and with fewer workgroups than chunks."""
+    import torch
+    from synth import gpu as SG
+    n = nbytes // 4
+    src = torch.randint(-2**31, 2**31 - 1, (n + 64,), dtype=torch.int32, device=gpu)
+    dst = torch.zeros(n + 64, dtype=torch.int32, device=gpu)
+    SG.probe_copy_capped(dst.data_ptr(), src.data_ptr(), nbytes, cap, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:n], src[:n]) and not torch.any(dst[n:])
