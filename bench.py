@@ -1274,9 +1274,10 @@ def main():
                 "frac": launch_bytes / (sum(fresh_nt_ms) / len(fresh_nt_ms) / 1e3) / 1e9 / HBM_PEAK_GBPS},
             "note": "not the timed region: each step right after a fresh 15 GB seeded refill of the gradients, "
                     "written with ordinary cached stores (ms_per_step) or with non-temporal stores "
-                    "(non_temporal_fill); cached stores to the addresses the step then reads leave its waves "
-                    "issuing the same loads more slowly (same L2 and DRAM traffic, lower fabric latency under "
-                    "counters); non-temporal stores, as the library's own producers use, leave no such cost"},
+                    "(non_temporal_fill); the fit to the measurements is that cached stores leave about one "
+                    "slice (~256 MB) of dirty lines in the memory-side Infinity Cache, written back among the "
+                    "step's reads (same L2 traffic under counters); non-temporal stores, as the library's own "
+                    "producers use, leave no such cost"},
     }
     del run
     torch.cuda.synchronize()
