@@ -836,6 +836,61 @@ def _stage3_cu_split(torch, run, t, nl, compute, compute_only, splits):
     return out
 
 
+def measure_slice_placement(torch, rounds=3):
+    """The fused 7.5B step with its 64 gradient slices copied into one pool at
+    a chosen distance apart: packed, the bench's own 256-byte-aligned rows,
+    the slice rounded up to whole MiB (224 MiB), and 256 MiB (a power of two)
+    plus small offsets.
+    Slices the same power-of-two distance apart are read at the same offset
+    at once, so the distance decides how the 64 streams spread over the
+    HBM channels.  Median over rounds of block-timed launches."""
+    import zero_sharded_mixed_02_amd as Z
+    from synth.workloads import WORKLOADS, GpuRun
+    run = GpuRun(WORKLOADS["7.5B-stage2"])
+    cfg, S, L0 = run.cfg, run.S, run.layers[0]
+    run.fill_grads(1)
+    MiB = 1 << 20
+    sb = 2 * S
+    strides = {"packed": sb, "bench_rows_256B": -(-S // 128) * 256,
+               "224MiB": 224 * MiB,   # the slice rounded up to whole MiB: 7 x 32 MiB
+               "256MiB": 256 * MiB}
+    for extra in (256, 1024, 2048, 4096, 65536):
+        strides[f"256MiB+{extra}B"] = 256 * MiB + extra
+    n = cfg.n_d
+    pool_bytes = max(strides.values()) * (n - 1) + sb
+    pool = torch.empty(pool_bytes // 2, dtype=torch.int16, device="cuda")
+    t = [5]
+
+    def step_for(stride):
+        for q in range(n):
+            pool[q * stride // 2:q * stride // 2 + S].copy_(L0["grads"][q])
+        torch.cuda.synchronize()
+        src = Z.GradSrc(cfg.gdt, [pool.data_ptr() + q * stride for q in range(n)])
+
+        def step():
+            t[0] += 1
+            Z.zero_adam_step(run.plan, cfg.owner, cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.grad_scale, t[0],
+                             src, None, L0["master"], L0["m"], L0["v"], run.full, cfg.pdt, True)
+        return step
+
+    times = {k: [] for k in strides}
+    for _ in range(rounds):
+        for name, stride in strides.items():
+            step = step_for(stride)
+            for _ in range(3):
+                step()
+            times[name].append(_time_launches(torch, step, reps=20, warmup=3))
+    out = {}
+    for name, v in times.items():
+        ms = sorted(v)[len(v) // 2]
+        out[name] = {"stride_bytes": strides[name], "ms": ms, "frac": 154 * S / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS}
+        log(f"slice placement {name}: stride {strides[name]} B, {ms:.4f} ms, frac {out[name]['frac']:.4f}")
+    del pool, run
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure_stage3_overlap(torch, splits=(16, 32, 64)):
     """The Stage-3 8-layer loop with a layer-compute stand-in: serial,
     prefetching on a second stream, and prefetching with the CUs split."""
@@ -1121,6 +1176,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels", action="store_true",
                     help="also time every entry point at its own workload (adds a 'kernels' object)")
+    ap.add_argument("--slice-placement", action="store_true",
+                    help="time the fused 7.5B step with its gradient slices at chosen distances apart "
+                         "(adds 'slice_placement')")
     ap.add_argument("--stage3-overlap", action="store_true",
                     help="also time the Stage-3 loop with a compute stand-in, serial, prefetching and with the "
                          "CUs split between compute and gather (adds 'stage3_overlap')")
@@ -1296,6 +1354,8 @@ def main():
         out["write_windows"] = measure_windows(torch)
     if args.stage3_overlap:
         out["stage3_overlap"] = measure_stage3_overlap(torch)
+    if args.slice_placement:
+        out["slice_placement"] = measure_slice_placement(torch)
     if args.no_cpu_baseline or args.headline_only:
         out["cpu_baseline"] = None
     else:

@@ -225,7 +225,11 @@ ZERO_API zero_status zero_shard_reduce(zero_plan_t plan, int32_t rank, const zer
  * stores slow it by about 12% on MI355X; written with non-temporal stores
  * (as zero_shard_reduce, zero_flatten and zero_gather_pack write their
  * outputs) they cost nothing.  A producer of the slices should store them
- * non-temporally.
+ * non-temporally.  Where the slices sit matters too: every wave reads the
+ * same offset of all n_d slices at once, and slices a power of two apart
+ * (say 256 MiB) put those reads on the same HBM channels, which costs the
+ * step 4-6%; staggering them by 1-4 KiB, or packing them back to back,
+ * avoids it.
  * Errors: EINVAL for a bad rank, t < 1, nulls, misalignment, src->n != n_d,
  * overlapping outputs; EUNSUPPORTED for non-16-bit types or for the fused
  * path with n_d > ZERO_MAX_RANKS (use zero_shard_reduce, then reduced).
