@@ -836,6 +836,66 @@ def _stage3_cu_split(torch, run, t, nl, compute, compute_only, splits):
     return out
 
 
+# Shapes the automatic window was not tuned on: (N_d, shard elements, gradient
+# dtype name).  Flat single-tensor plans, align 64, owner 0, fp16 parameters.
+WINDOW_SHAPES = ((16, 400_000_000, "fp16"), (24, 150_000_000, "bf16"), (32, 100_000_000, "bf16"),
+                 (32, 30_000_000, "bf16"), (40, 80_000_000, "bf16"), (48, 60_000_000, "bf16"),
+                 (64, 20_000_000, "bf16"), (64, 40_000_000, "bf16"), (96, 30_000_000, "bf16"),
+                 (128, 40_000_000, "bf16"))
+
+
+def measure_window_shapes(torch, rounds=3):
+    """The fused step on synthetic shapes outside the tuned workloads (other
+    rank counts and shard sizes): the automatic window against no window and
+    a grid of periods x opening shares.  Median over rounds that visit every
+    setting in turn; fractions of the HBM peak."""
+    import synth
+    import zero_sharded_mixed_02_amd as Z
+    from synth import gpu as SG
+    stream = torch.cuda.current_stream().cuda_stream
+    settings = [("auto", (-1, 0)), ("off", (0, 0))]
+    for per in (2000, 3000, 4000, 6000):
+        for share in (0.10, 0.17, 0.25, 0.35):
+            settings.append((f"{per}/{share:.2f}", (per, max(1, int(per * share)))))
+    out = {}
+    for n_d, shard, gname in WINDOW_SHAPES:
+        gdt = Z.ZERO_BF16 if gname == "bf16" else Z.ZERO_F16
+        psi = n_d * shard
+        plan = Z.zero_plan(psi, n_d, [psi], 0, 64)
+        S = plan.shard_total
+        g = torch.empty((n_d, S), dtype=torch.int16, device="cuda")
+        for q in range(n_d):
+            SG.fill(g[q].data_ptr(), gdt, S, synth.key_of(11, 1, q, 1), 0, 1e-3, stream, nt=True)
+        master = torch.empty(S, dtype=torch.float32, device="cuda")
+        SG.fill(master.data_ptr(), Z.ZERO_F32, S, synth.key_of(11, 2, 0, 0), 0, 0.02, stream, nt=True)
+        m, v = torch.zeros_like(master), torch.zeros_like(master)
+        full = torch.empty(plan.psi_pad, dtype=torch.int16, device="cuda")
+        src = Z.GradSrc(gdt, [g[q] for q in range(n_d)])
+        t = [0]
+
+        def step():
+            t[0] += 1
+            Z.zero_adam_step(plan, 0, 1e-4, 0.9, 0.999, 1e-8, 1.0 / n_d, t[0], src, None, master, m, v, full,
+                             Z.ZERO_F16, True)
+        nbytes = (2 * n_d + 26) * S
+        reps = max(4, min(20, int(3e10 / nbytes)))
+        times = {k: [] for k, _ in settings}
+        for _ in range(rounds):
+            for name, w in settings:
+                Z.zero_set_write_window(*w)
+                times[name].append(_time_launches(torch, step, reps=reps, warmup=2))
+        Z.zero_set_write_window(-1)
+        frac = {k: round(nbytes / (sorted(v)[len(v) // 2] / 1e3) / 1e9 / HBM_PEAK_GBPS, 4) for k, v in times.items()}
+        best = max((k for k in frac if k != "auto"), key=frac.get)
+        key = f"nd{n_d}_S{shard // 1_000_000}M_{gname}"
+        out[key] = {"frac_hbm_peak": frac, "best": best, "auto_over_best": round(frac["auto"] / frac[best], 4)}
+        log(f"window shape {key}: off {frac['off']:.3f}, auto {frac['auto']:.3f}, best {best} {frac[best]:.3f}")
+        del g, master, m, v, full, src, plan
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
 def measure_slice_placement(torch, rounds=3):
     """The fused 7.5B step with its 64 gradient slices copied into one pool at
     a chosen distance apart: packed, the bench's own 256-byte-aligned rows,
@@ -1176,6 +1236,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels", action="store_true",
                     help="also time every entry point at its own workload (adds a 'kernels' object)")
+    ap.add_argument("--window-shapes", action="store_true",
+                    help="the automatic write window against a grid on rank counts and shard sizes outside "
+                         "the tuned workloads (adds 'window_shapes')")
     ap.add_argument("--slice-placement", action="store_true",
                     help="time the fused 7.5B step with its gradient slices at chosen distances apart "
                          "(adds 'slice_placement')")
@@ -1354,6 +1417,8 @@ def main():
         out["write_windows"] = measure_windows(torch)
     if args.stage3_overlap:
         out["stage3_overlap"] = measure_stage3_overlap(torch)
+    if args.window_shapes:
+        out["window_shapes"] = measure_window_shapes(torch)
     if args.slice_placement:
         out["slice_placement"] = measure_slice_placement(torch)
     if args.no_cpu_baseline or args.headline_only:

@@ -464,10 +464,11 @@ int main() {
     check_reduce(p, 7, 0);
     zero_plan_destroy(p);
   }
-  // The automatic window of a large launch: 64 ranks, 2^25 + 4096 elements
-  // per shard (only the tables are built; no memory behind the pointers).
+  // The automatic window of a large launch: 64 ranks, 2^26 + 4096 elements
+  // per shard, 16 generations of resident workgroups (only the tables are
+  // built; no memory behind the pointers).
   {
-    std::vector<int64_t> sizes = {((int64_t)1 << 25) * 64 + 4096 * 64};
+    std::vector<int64_t> sizes = {((int64_t)1 << 26) * 64 + 4096 * 64};
     zero_plan_t p;
     zero_plan(sizes[0], 64, sizes.data(), 1, 0, 64, &p);
     g_steps.clear();
@@ -513,6 +514,38 @@ int main() {
              g_steps.empty() ? 0u : g_steps[0].a.win_open);
       zero_plan_destroy(p3);
     }
+    // Between 6 and 12 generations the period ramps from half to full: 8
+    // generations take 2/3 of it, 4107 ticks, open 373.  Other rank counts at
+    // 16 generations: the kernel for N_d = 32 (not compiled in) writes 14/90 of
+    // its bytes, above 12%, so it opens for 1.5 times that share; N_d = 48
+    // writes 14/122, below, and N_d = 16 (compiled in) keeps its written share.
+    {
+      struct Case {
+        int32_t n_d;
+        int64_t shard;
+        uint32_t period, open;
+        const char* what;
+      };
+      const Case cases[] = {{64, (int64_t)8 * 1024 * 4096, 4107, 373, "8-generation launch"},
+                            {32, (int64_t)16 * 1024 * 4096, 3600, 840, "N_d = 32 launch"},
+                            {48, (int64_t)16 * 1024 * 4096, 4880, 560, "N_d = 48 launch"},
+                            {16, (int64_t)16 * 1024 * 4096, 2320, 560, "N_d = 16 launch"}};
+      for (const Case& c : cases) {
+        std::vector<int64_t> sz = {c.shard * c.n_d};
+        zero_plan_t pc;
+        zero_plan(sz[0], c.n_d, sz.data(), 1, 0, 64, &pc);
+        zero_grad_src srcc = {ZERO_BF16, c.n_d, ptrs.data(), nullptr};
+        g_steps.clear();
+        EXPECT(zero_adam_step(pc, 1, &hp, 1, &srcc, nullptr, (float*)(uintptr_t)fake_base(1),
+                              (float*)(uintptr_t)fake_base(2), (float*)(uintptr_t)fake_base(3),
+                              (void*)(uintptr_t)fake_base(4), ZERO_F16, 1, nullptr) == ZERO_OK,
+               "%s failed: %s", c.what, zero_last_error());
+        EXPECT(g_steps.size() == 1 && g_steps[0].a.win_period == c.period && g_steps[0].a.win_open == c.open,
+               "automatic window of a %s: (%u, %u)", c.what, g_steps.empty() ? 0u : g_steps[0].a.win_period,
+               g_steps.empty() ? 0u : g_steps[0].a.win_open);
+        zero_plan_destroy(pc);
+      }
+    }
     // Few ranks: no automatic window.
     std::vector<int64_t> s8 = {((int64_t)1 << 25) * 8};
     zero_plan_t p8;
@@ -531,7 +564,7 @@ int main() {
   // Scope of the setting: a stream's own setting wins on that stream only;
   // -2 returns the stream to the process-wide default.
   {
-    std::vector<int64_t> sizes = {((int64_t)1 << 25) * 64};
+    std::vector<int64_t> sizes = {((int64_t)1 << 26) * 64};
     zero_plan_t p;
     zero_plan(sizes[0], 64, sizes.data(), 1, 0, 64, &p);
     std::vector<const void*> ptrs(64);

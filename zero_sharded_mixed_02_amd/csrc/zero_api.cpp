@@ -175,17 +175,27 @@ bool encode_window(int64_t period_ticks, int64_t open_ticks, uint64_t& w) {
 // resident workgroups takes to stream its bytes at ~6.5 TB/s, and the best
 // opening near the written share of the bytes (at least 1/16 of the period).
 // Launches with few ranks per written element or few elements gain nothing.
-// A launch of only a few generations (a Stage-3 layer is three) does better
-// with a proportionally shorter period: its waits at the end are not hidden
-// by later generations.  The streaming rate is a fixed share of the HBM peak
-// the device reports (memory clock x 4 transfers x bus width: 8.19 TB/s on
-// MI355X, 5.3 TB/s on MI300X), and periods are converted to ticks with the
-// rate the device reports for its real-time counter.
+// A launch of few generations does better with a shorter period: its waits at
+// the end are not hidden by later generations.  Up to 6 generations take at
+// most half the period (a Stage-3 layer is three), and the full period is
+// reached at 12.  The kernel for rank counts that are not compiled in (other
+// than 4, 8, 16, 64) does better with an opening of 1.5 times the written
+// share once that share passes 12% (N_d below ~44): 2-5% at N_d = 24 and 32,
+// where the written share alone left its waves waiting.  The last two rules
+// come from a same-process comparison over 14 shapes (N_d 16-128, shards of
+// 20M-812M elements); neither changes the window of the workloads above.  The
+// streaming rate is a fixed share of the HBM peak the device reports (memory
+// clock x 4 transfers x bus width: 8.19 TB/s on MI355X, 5.3 TB/s on MI300X),
+// and periods are converted to ticks with the rate the device reports for its
+// real-time counter.
 constexpr int kAutoMinRanks = 16;
-constexpr double kAutoFullGenerations = 6.0;
+constexpr double kAutoShortGenerations = 6.0;
+constexpr double kAutoFullGenerations = 12.0;
 constexpr int64_t kAutoMinElems = int64_t(1) << 23;
 constexpr double kAutoStreamShare = 6.5e12 / 8.192e12;   // 6.5 TB/s on MI355X
 constexpr double kAutoPeriodShare = 0.62;                 // of one generation's streaming time
+constexpr double kAutoWideOpeningShare = 0.12;            // generic kernel: written share above which
+constexpr double kAutoWideOpening = 1.5;                  //   the opening is this multiple of it
 
 void auto_window(int mode, int gdt, int pdt, int ndc, int n_ranks, int64_t elems, int64_t blocks,
                  zk::StepArgs& a) {
@@ -199,10 +209,16 @@ void auto_window(int mode, int gdt, int pdt, int ndc, int n_ranks, int64_t elems
   const double written = mode == zk::kFused ? 14.0 : 4.0;
   const double gen_bytes = (double)resident * zk::kStepThreads * zk::kStepVec * (read + written);
   double period = gen_bytes / (kAutoStreamShare * peak) * kAutoPeriodShare * hz;
-  period *= std::min(1.0, (double)blocks / resident / kAutoFullGenerations);
+  const double gens = (double)blocks / resident;
+  period *= gens < kAutoShortGenerations
+                ? std::min(0.5, gens / kAutoShortGenerations)
+                : std::min(1.0, 0.5 + 0.5 * (gens - kAutoShortGenerations) /
+                                          (kAutoFullGenerations - kAutoShortGenerations));
   const double min_period = 2e-6 * hz;   // 2 us
   period = std::min<double>(std::max(period, min_period), (double)zk::kMaxWindowPeriod);
-  const double open = period * std::max(written / (read + written), 1.0 / 16.0);
+  const double w_share = written / (read + written);
+  const double o_share = ndc == 0 && w_share > kAutoWideOpeningShare ? kAutoWideOpening * w_share : w_share;
+  const double open = period * std::min(0.5, std::max(o_share, 1.0 / 16.0));
   a.win_period = (uint32_t)period;
   a.win_open = std::max<uint32_t>(1, std::min<uint32_t>((uint32_t)open, a.win_period));
 }
