@@ -354,7 +354,37 @@ __global__ void __launch_bounds__(kStepThreads) step_vec_kernel(const StepArgs a
 
   float g[8];
   if constexpr (MODE == kFromReduced) {
-    load_groups(a.reduced + shard_off, ea, eb, g);
+    // About one byte written per byte read, as in a copy: group by group (load
+    // the lane's 4 elements of every array, update, store, then the next 4),
+    // so a lane has 64 bytes of loads in flight rather than 128.  A plain
+    // copy runs fastest at that depth on MI355X; here it is ~1% faster than
+    // both groups at once, and the arithmetic is the same.
+    const AdamC k = load_consts(a);
+    gu32x2* const dp = gaddr<gu32x2*>((uint16_t*)a.dst + dst_off);
+    auto group = [&](uint32_t e) {
+      const f32x4 g4 = ld_nt(gaddr<const gf32x4*>(a.reduced + shard_off) + (e >> 2));
+      const f32x4 w4 = ld_nt(gaddr<const gf32x4*>(a.master + shard_off) + (e >> 2));
+      const f32x4 m4 = ld_nt(gaddr<const gf32x4*>(a.m + shard_off) + (e >> 2));
+      const f32x4 v4 = ld_nt(gaddr<const gf32x4*>(a.v + shard_off) + (e >> 2));
+      float w[4], m[4], v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        w[i] = w4[i];
+        m[i] = m4[i];
+        v[i] = v4[i];
+        adam1(k, g4[i], w[i], m[i], v[i]);
+      }
+      st_nt(gaddr<gf32x4*>(a.master + shard_off) + (e >> 2), f32x4{w[0], w[1], w[2], w[3]});
+      st_nt(gaddr<gf32x4*>(a.m + shard_off) + (e >> 2), f32x4{m[0], m[1], m[2], m[3]});
+      st_nt(gaddr<gf32x4*>(a.v + shard_off) + (e >> 2), f32x4{v[0], v[1], v[2], v[3]});
+      st_nt(dp + (e >> 2), u32x2{narrow1<PDT>(w[0]) | (narrow1<PDT>(w[1]) << 16),
+                                 narrow1<PDT>(w[2]) | (narrow1<PDT>(w[3]) << 16)});
+    };
+    group(ea);
+    if (vb) group(eb);
+    if (tb)
+      for (uint32_t e = ea + kHalf; e < len; ++e) step_one<MODE, GDT, PDT>(a, shard_off, full_off, dst_off, e);
+    return;
   } else if constexpr (MODE == kFused) {
     float acc[8];
     fold<GDT, NDC, false>(a, shard_off, full_off, ea * 2u, eb * 2u, acc);
