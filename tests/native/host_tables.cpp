@@ -134,6 +134,30 @@ int launch_copy(const CopyArgs& a, int esz, int n_blocks, void*) {
   return 0;
 }
 
+// Warm-up reads: recorded, and checked for a consistent workgroup layout.
+struct WarmRec {
+  WarmArgs a;
+  int blocks;
+};
+std::vector<WarmRec> g_warms;
+int launch_warm(const WarmArgs& a, int n_blocks, void*) {
+  if (g_inject_error) {
+    const int e = g_inject_error;
+    g_inject_error = 0;
+    return e;
+  }
+  EXPECT(a.n >= 1 && a.n <= kWarmRanges, "warm-up with %d ranges", a.n);
+  int64_t b = 0;
+  for (int i = 0; i < a.n; ++i) {
+    EXPECT(a.block_start[i] == b, "warm-up range %d starts at workgroup %d, not %lld", i, a.block_start[i], (long long)b);
+    EXPECT(a.units[i] > 0 && ((uintptr_t)a.base[i] & 15) == 0, "warm-up range %d empty or misaligned", i);
+    b += (a.units[i] + kWarmThreads * kWarmUnits - 1) / (kWarmThreads * kWarmUnits);
+  }
+  EXPECT(b == n_blocks, "warm-up launches %d workgroups for %lld", n_blocks, (long long)b);
+  g_warms.push_back(WarmRec{a, n_blocks});
+  return 0;
+}
+
 int launch_step(const StepArgs& a, int mode, int gdt, int pdt, int ndc, bool vec, int n_blocks, void*) {
   if (g_inject_error) {
     const int e = g_inject_error;
@@ -560,6 +584,74 @@ int main() {
     zero_plan_destroy(p8);
     (void)q;
     zero_plan_destroy(p);
+  }
+  // Warm-up read before the fused step (zero_set_warm_read): off by default;
+  // when on, only when the launch reads >= 1 GiB of gradients and the state
+  // is 16-byte aligned; 256 MiB of the state, master first; never before the
+  // reduction or Adam from the reduced gradient.
+  {
+    zero_adam_hyper hp = {1e-4, 0.9, 0.999, 1e-8, 1.0 / 64};
+    std::vector<const void*> ptrs(64);
+    for (int r = 0; r < 64; ++r) ptrs[r] = (const void*)(uintptr_t)fake_base(100 + r);
+    auto warms_for = [&](int32_t n_d, int64_t shard, uint64_t state_shift) {
+      std::vector<int64_t> sz = {shard * n_d};
+      zero_plan_t pw;
+      zero_plan(sz[0], n_d, sz.data(), 1, 0, 64, &pw);
+      zero_grad_src sw = {ZERO_BF16, n_d, ptrs.data(), nullptr};
+      zk::g_warms.clear();
+      g_steps.clear();
+      EXPECT(zero_adam_step(pw, 0, &hp, 1, &sw, nullptr, (float*)(uintptr_t)(fake_base(1) + state_shift),
+                            (float*)(uintptr_t)(fake_base(2) + state_shift),
+                            (float*)(uintptr_t)(fake_base(3) + state_shift), (void*)(uintptr_t)fake_base(4),
+                            ZERO_F16, 1, nullptr) == ZERO_OK,
+             "warm-up case step failed: %s", zero_last_error());
+      zero_plan_destroy(pw);
+      return zk::g_warms;
+    };
+    // Off by default; 0 and 1 only.
+    EXPECT(warms_for(64, (int64_t)1 << 26, 0).empty(), "warm-up read on by default");
+    EXPECT(zero_set_warm_read(2) == ZERO_EINVAL && zero_set_warm_read(-1) == ZERO_EINVAL, "warm-up setting 2 or -1 accepted");
+    EXPECT(zero_set_warm_read(1) == ZERO_OK, "warm-up setting refused");
+    // 7.5B-like: 64 ranks x 2^26 elements (8.6 GB of gradients): 256 MiB of master only.
+    auto w1 = warms_for(64, (int64_t)1 << 26, 0);
+    EXPECT(w1.size() == 1 && w1[0].a.n == 1 && w1[0].a.base[0] == (const void*)(uintptr_t)fake_base(1) &&
+               w1[0].a.units[0] == ((int64_t)256 << 20) / 16 && w1[0].blocks == 2048,
+           "warm-up of a large launch: %zu launches", w1.size());
+    // A Stage-3 layer (64 x 12,584,576; 1.6 GB of gradients): all of master, m and v (151 MB).
+    auto w2 = warms_for(64, 12584576, 0);
+    EXPECT(w2.size() == 1 && w2[0].a.n == 3 && w2[0].a.units[0] == (int64_t)12584576 * 4 / 16 &&
+               w2[0].a.units[2] == (int64_t)12584576 * 4 / 16 &&
+               w2[0].a.base[2] == (const void*)(uintptr_t)fake_base(3),
+           "warm-up of a Stage-3 layer: %zu launches", w2.size());
+    // Small launches (8 ranks x 15.5M elements: 0.25 GB) and misaligned state: none.
+    EXPECT(warms_for(8, 15456576, 0).empty(), "warm-up of a small launch");
+    EXPECT(warms_for(64, (int64_t)1 << 26, 4).empty(), "warm-up with state not 16-byte aligned");
+    // The warm-up's launch error is reported, and no step is launched after it.
+    g_inject_error = 703;
+    {
+      std::vector<int64_t> sz = {((int64_t)1 << 26) * 64};
+      zero_plan_t pw;
+      zero_plan(sz[0], 64, sz.data(), 1, 0, 64, &pw);
+      zero_grad_src sw = {ZERO_BF16, 64, ptrs.data(), nullptr};
+      g_steps.clear();
+      EXPECT(zero_adam_step(pw, 0, &hp, 1, &sw, nullptr, (float*)(uintptr_t)fake_base(1),
+                            (float*)(uintptr_t)fake_base(2), (float*)(uintptr_t)fake_base(3),
+                            (void*)(uintptr_t)fake_base(4), ZERO_F16, 1, nullptr) == ZERO_EHIP &&
+                 g_steps.empty(),
+             "warm-up launch error not reported");
+      // Neither the reduction nor Adam from the reduced gradient warms up.
+      zk::g_warms.clear();
+      EXPECT(zero_shard_reduce(pw, 0, &sw, 1.0 / 64, (float*)(uintptr_t)fake_base(5), nullptr) == ZERO_OK,
+             "reduce failed: %s", zero_last_error());
+      EXPECT(zero_adam_step(pw, 0, &hp, 1, nullptr, (const float*)(uintptr_t)fake_base(5),
+                            (float*)(uintptr_t)fake_base(1), (float*)(uintptr_t)fake_base(2),
+                            (float*)(uintptr_t)fake_base(3), (void*)(uintptr_t)fake_base(4), ZERO_F16, 1,
+                            nullptr) == ZERO_OK, "from-reduced step failed: %s", zero_last_error());
+      EXPECT(zk::g_warms.empty(), "warm-up before the reduction or Adam from the reduced gradient");
+      zero_plan_destroy(pw);
+    }
+    EXPECT(zero_set_warm_read(0) == ZERO_OK, "warm-up setting refused");
+    EXPECT(warms_for(64, (int64_t)1 << 26, 0).empty(), "warm-up read after turning it off");
   }
   // Scope of the setting: a stream's own setting wins on that stream only;
   // -2 returns the stream to the process-wide default.

@@ -34,6 +34,10 @@ int launch_copy(const CopyArgs& a, int, int n_blocks, void*) {
   g_copy_launches++;
   return 0;
 }
+int launch_warm(const WarmArgs& a, int n_blocks, void*) {
+  if (a.n < 1 || n_blocks < 1) g_fail++;
+  return 0;
+}
 const char* hip_error_string(int) { return "stand-in"; }
 int resident_blocks(int, int, int, int, bool) { return 1024; }
 double wall_clock_hz() { return 1e8; }
@@ -105,6 +109,7 @@ int main() {
       void* s = (void*)(uintptr_t)(0x100 * (1 + i % 4));
       if (i % 5 == 0) zero_set_stream_write_window(s, -2, 0);
       else zero_set_stream_write_window(s, i % 2 ? 0 : 2000, 200);
+      zero_set_warm_read(i % 3 == 0);
     }
   });
   std::vector<std::thread> ts;

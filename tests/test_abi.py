@@ -263,6 +263,15 @@ def test_write_window_setting(zero_lib):
         Z.zero_set_stream_write_window(0x1234, *good)
 
 
+def test_warm_read_setting(zero_lib):
+    """zero_set_warm_read accepts 0 and 1 only (no launch involved)."""
+    Z = zero_lib
+    for bad in (2, -1):
+        assert Z.load().zero_set_warm_read(bad) == Z.ZERO_EINVAL
+    for good in (True, False):
+        Z.zero_set_warm_read(good)
+
+
 def test_flatten_needs_no_workspace(zero_lib):
     Z = zero_lib
     for sizes, cap in (([10], 0), ([5, 0, 7000, 3], 100), (list(range(1, 300)), 50)):

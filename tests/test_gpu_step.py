@@ -213,6 +213,39 @@ def test_write_windows_change_nothing(gpu, oracle_lib, zero_lib, window):
         Z.zero_set_write_window(-1)
 
 
+def test_warm_read_changes_nothing(gpu, zero_lib):
+    """zero_set_warm_read(1) adds a read of the state before fused steps that
+    read >= 1 GiB of gradients (here 64 ranks x 8.5M elements, 1.09 GB) and
+    leaves every result bit unchanged: two steps from the same state with the
+    warm-up on and off give identical master, m, v and parameters, right
+    after gradients written with ordinary stores (the case it is for).  The
+    path without it is checked against the oracle by the other tests."""
+    import torch
+    Z = zero_lib
+    cfg = small_config(64 * 8_500_000, 64, BF16, F16, owner=5, steps=2, seed=41, align=64)
+    say("[warm read] 64 ranks x 8.5M, on and off, 2 steps")
+    run = GpuRun(cfg)
+    L0 = run.layers[0]
+    start = [L0[k].clone() for k in ("master", "m", "v")]
+    out = {}
+    try:
+        for warm in (False, True):
+            Z.zero_set_warm_read(warm)
+            for k, x in zip(("master", "m", "v"), start):
+                L0[k].copy_(x)
+            run.full.zero_()
+            for t in (1, 2):
+                run.fill_grads(t)
+                run.step(t)
+            _sync()
+            out[warm] = [L0[k].clone() for k in ("master", "m", "v")] + [run.full.clone()]
+    finally:
+        Z.zero_set_warm_read(False)
+    for name, a, b in zip(("master", "m", "v", "params"), out[False], out[True]):
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
+                           b.view(torch.int32) if b.dtype == torch.float32 else b), name
+
+
 def test_stream_write_window_changes_nothing(gpu, oracle_lib, zero_lib):
     """A window set for one stream only (zero_set_stream_write_window) applies
     to launches on that stream and leaves every result bit unchanged; the

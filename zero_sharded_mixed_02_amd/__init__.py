@@ -36,7 +36,7 @@ STATUS_NAMES = {0: "ZERO_OK", -1: "ZERO_EINVAL", -2: "ZERO_EUNSUPPORTED", -3: "Z
 ENTRY_POINTS = ("zero_version", "zero_last_error", "zero_plan", "zero_plan_destroy",
                 "zero_plan_info", "zero_plan_bucket", "zero_plan_tensor", "zero_flatten_workspace_bytes",
                 "zero_flatten", "zero_shard_reduce", "zero_adam_step", "zero_gather_pack", "zero_reshard",
-                "zero_set_write_window", "zero_set_stream_write_window")
+                "zero_set_write_window", "zero_set_stream_write_window", "zero_set_warm_read")
 
 
 class ZeroError(RuntimeError):
@@ -112,6 +112,8 @@ def load():
     L.zero_set_write_window.argtypes = [i64, i64]
     L.zero_set_stream_write_window.restype = i32
     L.zero_set_stream_write_window.argtypes = [vp, i64, i64]
+    L.zero_set_warm_read.restype = i32
+    L.zero_set_warm_read.argtypes = [i32]
     _lib = L
     return L
 
@@ -221,6 +223,12 @@ def zero_set_stream_write_window(stream, period_ticks: int, open_ticks: int = 0)
     """The same setting for launches on one stream only; -2 removes the
     stream's own setting so it follows the process-wide default again."""
     _check(load().zero_set_stream_write_window(_stream(stream), period_ticks, open_ticks))
+
+
+def zero_set_warm_read(enable: bool) -> None:
+    """Read up to 256 MiB of the fused step's own state just before each
+    large fused step (process-wide; off by default)."""
+    _check(load().zero_set_warm_read(1 if enable else 0))
 
 
 def zero_last_error() -> str:

@@ -85,6 +85,18 @@ struct CopyArgs {
   CopyEnt ent[kMaxCopy];
 };
 
+// Ranges of the fused step's own fp32 state read ahead of it with ordinary
+// (cached) loads; nothing is written.  See warm_kernel in zero_kernels.hip.
+constexpr int kWarmRanges = 3;
+constexpr int kWarmThreads = 1024;   // workgroup
+constexpr int kWarmUnits = 8;        // 16-byte loads per lane
+struct WarmArgs {
+  const void* base[kWarmRanges];      // 16-byte aligned
+  int64_t units[kWarmRanges];         // 16-byte units of each range
+  int32_t block_start[kWarmRanges];   // first workgroup of each range
+  int32_t n;                          // ranges in use
+};
+
 static_assert(sizeof(StepArgs) <= 4096, "step kernel arguments must fit 4 KiB");
 static_assert(sizeof(CopyArgs) <= 4096, "copy kernel arguments must fit 4 KiB");
 
@@ -92,6 +104,7 @@ static_assert(sizeof(CopyArgs) <= 4096, "copy kernel arguments must fit 4 KiB");
 int launch_step(const StepArgs& a, int mode, int gdt, int pdt, int ndc, bool vec, int n_blocks,
                 void* stream);
 int launch_copy(const CopyArgs& a, int esz, int n_blocks, void* stream);
+int launch_warm(const WarmArgs& a, int n_blocks, void* stream);
 const char* hip_error_string(int err);
 // Workgroups of the chosen step kernel that the current device holds at once
 // (blocks per CU at the kernel's register use x CUs); 0 if unknown.

@@ -581,6 +581,48 @@ __global__ void __launch_bounds__(kThreads) copy_kernel(const CopyArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Warm-up read before the fused step
+// ---------------------------------------------------------------------------
+
+// Reads the given ranges of the step's fp32 state with ordinary (cached)
+// loads and stores nothing; an empty asm takes each loaded value, so the
+// loads are kept.  Run just before a large fused step it does two things on
+// MI355X: the lines it brings into the 256 MB memory-side Infinity Cache push
+// out what a producer of the gradients left there dirty (ordinary stores of
+// the last ~256 MB written), so those write-backs happen now rather than
+// among the step's reads; and the step then finds this part of its state in
+// that cache.  After gradients written with ordinary stores the step is ~11%
+// faster (7.5B, N_d = 64); after a step, or gradients written non-temporally,
+// the read repays its own time.  Full workgroups take every unit without
+// per-unit checks (wave w reads the workgroup's w-th 64 x kWarmUnits units
+// as 1 KiB spans); the last workgroup of a range checks each unit.
+__global__ void __launch_bounds__(kWarmThreads) warm_kernel(const WarmArgs a) {
+  const int blk = blockIdx.x;
+  int r = 0;
+  for (int i = 1; i < a.n; ++i)
+    if (a.block_start[i] <= blk) r = i;
+  const int64_t units = a.units[r];
+  const int64_t first = (int64_t)(blk - a.block_start[r]) * (kWarmThreads * kWarmUnits);
+  const gu32x4* const p = gaddr<const gu32x4*>(a.base[r]);
+  if (first + kWarmThreads * kWarmUnits <= units) {
+    const gu32x4* const wv = p + first + (threadIdx.x >> 6) * (64 * kWarmUnits) + (threadIdx.x & 63);
+    u32x4 x[kWarmUnits];
+#pragma unroll
+    for (int i = 0; i < kWarmUnits; ++i) x[i] = wv[i * 64];
+#pragma unroll
+    for (int i = 0; i < kWarmUnits; ++i) asm volatile("" ::"v"(x[i]));
+  } else {
+    for (int i = 0; i < kWarmUnits; ++i) {
+      const int64_t u = first + threadIdx.x + (int64_t)i * kWarmThreads;
+      if (u < units) {
+        const u32x4 x = p[u];
+        asm volatile("" ::"v"(x));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Dispatch
 // ---------------------------------------------------------------------------
 
@@ -633,6 +675,12 @@ int launch_copy(const CopyArgs& a, int esz, int n_blocks, void* stream) {
   void* fn = esz == 2 ? (void*)&copy_kernel<2> : (void*)&copy_kernel<4>;
   void* args[] = {(void*)&a};
   return (int)hipLaunchKernel(fn, dim3((unsigned)n_blocks), dim3(kThreads), args, 0,
+                              (hipStream_t)stream);
+}
+
+int launch_warm(const WarmArgs& a, int n_blocks, void* stream) {
+  void* args[] = {(void*)&a};
+  return (int)hipLaunchKernel((void*)&warm_kernel, dim3((unsigned)n_blocks), dim3(kWarmThreads), args, 0,
                               (hipStream_t)stream);
 }
 
