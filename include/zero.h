@@ -308,21 +308,23 @@ ZERO_API zero_status zero_reshard(zero_plan_t src_plan, zero_plan_t dst_plan, in
 ZERO_API zero_status zero_set_write_window(int64_t period_ticks, int64_t open_ticks);
 
 /*
- * zero_set_warm_read -- a read of the fused step's own state just before it
+ * zero_set_warm_read -- a read of the step's own buffers just before it
  * (not an operation of the pages: a tuning knob of this library; results are
  * bit-identical whether it is on or off).  With enable = 1, every fused
- * zero_adam_step that reads at least 1 GiB of gradients first reads up to
- * 256 MiB of its fp32 state (master, then m, then v) with ordinary cached
- * loads, on the same stream, storing nothing.  MI355X's 256 MB memory-side
+ * zero_adam_step and every zero_shard_reduce that reads at least 1 GiB of
+ * gradients first reads up to 256 MiB of its fp32 state (master, then m, then
+ * v) or of its fp32 output with ordinary cached loads, on the same stream,
+ * storing nothing.  MI355X's 256 MB memory-side
  * Infinity Cache keeps the last lines written with ordinary stores dirty;
  * when the gradient slices were just written that way (as a collective or a
  * backward kernel may write them), their write-backs otherwise fall among the
  * step's reads and cost it ~12% (7.5B, N_d = 64).  The warm-up read moves them
  * before the step: measured, the step is then ~11% faster (7.5% for a Stage-3
- * layer, 3% for 13B at N_d = 16).  When the slices are already clean (written
- * non-temporally, as zero_shard_reduce and the copies write) it costs the
- * step 1-2%.  enable = 0 (the default): no warm-up read.  The state arrays
- * must be 16-byte aligned for it to run.  Process-wide; read by calls issued
+ * layer, 3% for 13B at N_d = 16), and the reduction ~11%.  When the slices are
+ * already clean (written non-temporally, as zero_shard_reduce and the copies
+ * write) it costs the step 1-2% and the reduction 2%.  enable = 0 (the
+ * default): no warm-up read.  The buffers read must be 16-byte aligned for it
+ * to run.  Process-wide; read by calls issued
  * after it, from any thread.  Errors: EINVAL for any other value.
  */
 ZERO_API zero_status zero_set_warm_read(int32_t enable);

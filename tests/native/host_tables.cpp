@@ -585,10 +585,10 @@ int main() {
     (void)q;
     zero_plan_destroy(p);
   }
-  // Warm-up read before the fused step (zero_set_warm_read): off by default;
-  // when on, only when the launch reads >= 1 GiB of gradients and the state
-  // is 16-byte aligned; 256 MiB of the state, master first; never before the
-  // reduction or Adam from the reduced gradient.
+  // Warm-up read (zero_set_warm_read): off by default; when on, only when the
+  // launch reads >= 1 GiB of gradients and the buffers are 16-byte aligned;
+  // 256 MiB of the fused step's state (master first) or of the reduction's
+  // output; never before Adam from the reduced gradient.
   {
     zero_adam_hyper hp = {1e-4, 0.9, 0.999, 1e-8, 1.0 / 64};
     std::vector<const void*> ptrs(64);
@@ -639,15 +639,21 @@ int main() {
                             (void*)(uintptr_t)fake_base(4), ZERO_F16, 1, nullptr) == ZERO_EHIP &&
                  g_steps.empty(),
              "warm-up launch error not reported");
-      // Neither the reduction nor Adam from the reduced gradient warms up.
+      // The reduction warms up 256 MiB of its own output; Adam from the
+      // reduced gradient (whose input the library wrote non-temporally) does not.
       zk::g_warms.clear();
       EXPECT(zero_shard_reduce(pw, 0, &sw, 1.0 / 64, (float*)(uintptr_t)fake_base(5), nullptr) == ZERO_OK,
              "reduce failed: %s", zero_last_error());
+      EXPECT(zk::g_warms.size() == 1 && zk::g_warms[0].a.n == 1 &&
+                 zk::g_warms[0].a.base[0] == (const void*)(uintptr_t)fake_base(5) &&
+                 zk::g_warms[0].a.units[0] == ((int64_t)256 << 20) / 16,
+             "warm-up before the reduction: %zu launches", zk::g_warms.size());
+      zk::g_warms.clear();
       EXPECT(zero_adam_step(pw, 0, &hp, 1, nullptr, (const float*)(uintptr_t)fake_base(5),
                             (float*)(uintptr_t)fake_base(1), (float*)(uintptr_t)fake_base(2),
                             (float*)(uintptr_t)fake_base(3), (void*)(uintptr_t)fake_base(4), ZERO_F16, 1,
                             nullptr) == ZERO_OK, "from-reduced step failed: %s", zero_last_error());
-      EXPECT(zk::g_warms.empty(), "warm-up before the reduction or Adam from the reduced gradient");
+      EXPECT(zk::g_warms.empty(), "warm-up before Adam from the reduced gradient");
       zero_plan_destroy(pw);
     }
     EXPECT(zero_set_warm_read(0) == ZERO_OK, "warm-up setting refused");

@@ -214,11 +214,12 @@ def test_write_windows_change_nothing(gpu, oracle_lib, zero_lib, window):
 
 
 def test_warm_read_changes_nothing(gpu, zero_lib):
-    """zero_set_warm_read(1) adds a read of the state before fused steps that
-    read >= 1 GiB of gradients (here 64 ranks x 8.5M elements, 1.09 GB) and
-    leaves every result bit unchanged: two steps from the same state with the
-    warm-up on and off give identical master, m, v and parameters, right
-    after gradients written with ordinary stores (the case it is for).  The
+    """zero_set_warm_read(1) adds a read of the state (or of the reduction's
+    output) before fused steps and reductions that read >= 1 GiB of gradients
+    (here 64 ranks x 8.5M elements, 1.09 GB) and leaves every result bit
+    unchanged: two steps and a reduction from the same state with the warm-up
+    on and off give identical master, m, v, parameters and reduced gradient,
+    right after gradients written with ordinary stores (the case it is for).  The
     path without it is checked against the oracle by the other tests."""
     import torch
     Z = zero_lib
@@ -227,6 +228,7 @@ def test_warm_read_changes_nothing(gpu, zero_lib):
     run = GpuRun(cfg)
     L0 = run.layers[0]
     start = [L0[k].clone() for k in ("master", "m", "v")]
+    red = torch.empty(run.S, dtype=torch.float32, device=gpu)
     out = {}
     try:
         for warm in (False, True):
@@ -237,11 +239,14 @@ def test_warm_read_changes_nothing(gpu, zero_lib):
             for t in (1, 2):
                 run.fill_grads(t)
                 run.step(t)
+            run.fill_grads(3)
+            red.fill_(-1.0)
+            run.reduce(red)
             _sync()
-            out[warm] = [L0[k].clone() for k in ("master", "m", "v")] + [run.full.clone()]
+            out[warm] = [L0[k].clone() for k in ("master", "m", "v")] + [run.full.clone(), red.clone()]
     finally:
         Z.zero_set_warm_read(False)
-    for name, a, b in zip(("master", "m", "v", "params"), out[False], out[True]):
+    for name, a, b in zip(("master", "m", "v", "params", "reduced"), out[False], out[True]):
         assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
                            b.view(torch.int32) if b.dtype == torch.float32 else b), name
 

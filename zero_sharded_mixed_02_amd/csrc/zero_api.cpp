@@ -316,29 +316,30 @@ zero_status check_plan(zero_plan_t p) {
   return ok();
 }
 
-// Warm-up read before a large fused step (warm_kernel), when enabled with
-// zero_set_warm_read: as much of the step's own fp32 state as MI355X's
-// Infinity Cache holds (256 MiB), master first, then m and v.  Only for
-// launches that read at least 1 GiB of gradients.  Measured on MI355X: right
-// after gradients written with ordinary stores the step is ~11% faster
-// (7.5B, N_d = 64; 7.5% for a Stage-3 layer, 3% for 13B); when the gradients
-// are already clean (written non-temporally, or steps back to back) it costs
-// 1-2%.  Small launches (GPT-2's 0.25 GB) lose either way, and the reduction,
-// which does not read the state again, loses 2%; neither warms up.
+// Warm-up read before a large fused step or reduction (warm_kernel), when
+// enabled with zero_set_warm_read: as much as MI355X's Infinity Cache holds
+// (256 MiB) of the step's own fp32 state (master first, then m and v), or of
+// the reduction's fp32 output.  Only for launches that read at least 1 GiB of
+// gradients.  Measured on MI355X: right after gradients written with ordinary
+// stores the step is ~11% faster (7.5B, N_d = 64; 7.5% for a Stage-3 layer,
+// 3% for 13B) and the reduction ~11%; when the gradients are already clean
+// (written non-temporally, or launches back to back) it costs the step 1-2%
+// and the reduction, which does not read those lines again, 2%.  Small
+// launches (GPT-2's 0.25 GB) lose either way and never warm up.
 constexpr int64_t kWarmBytes = int64_t(256) << 20;
 constexpr int64_t kWarmMinGradBytes = int64_t(1) << 30;
 std::atomic<int> g_warm{0};
 
-zero_status warm_state(float* const st[3], int64_t S, int32_t n_d, void* stream) {
+zero_status warm_state(float* const* st, int n_st, int64_t S, int32_t n_d, void* stream) {
   if (!g_warm.load(std::memory_order_relaxed)) return ok();
   if (2 * (int64_t)n_d * S < kWarmMinGradBytes) return ok();
-  for (int i = 0; i < 3; ++i)
+  for (int i = 0; i < n_st; ++i)
     if (!aligned(st[i], 16)) return ok();
   zk::WarmArgs w;
   memset(&w, 0, sizeof w);
   const int64_t per_block = (int64_t)zk::kWarmThreads * zk::kWarmUnits;
   int64_t left = kWarmBytes, blocks = 0;
-  for (int i = 0; i < zk::kWarmRanges && left >= 16; ++i) {
+  for (int i = 0; i < std::min(n_st, zk::kWarmRanges) && left >= 16; ++i) {
     const int64_t units = std::min<int64_t>(left, S * 4) / 16;
     if (units <= 0) continue;
     w.base[w.n] = st[i];
@@ -690,6 +691,7 @@ zero_status zero_shard_reduce(zero_plan_t p, int32_t rank, const zero_grad_src* 
     memset(&a, 0, sizeof a);
     a.out = out;
     a.c[8] = (float)grad_scale;
+    if (zero_status st = warm_state(&out, 1, p->shard_total, p->n_d, stream)) return st;
     // Ranks beyond one launch's table: later launches continue from out.
     for (int q0 = 0; q0 < p->n_d; q0 += zk::kMaxRanks) {
       const int n = std::min(zk::kMaxRanks, p->n_d - q0);
@@ -764,7 +766,7 @@ zero_status zero_adam_step(zero_plan_t p, int32_t rank, const zero_adam_hyper* h
     a.dst = param_dst;
     if (slices) {
       set_ranks(a, *slices, 0, p->n_d);
-      if (zero_status st = warm_state(st_ptr, S, p->n_d, stream)) return st;
+      if (zero_status st = warm_state(st_ptr, 3, S, p->n_d, stream)) return st;
       return run_step_all(a, ps, zk::kFused, slices->dtype, param_dt, vec_ok, uses_full, stream);
     }
     a.reduced = reduced;
