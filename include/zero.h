@@ -283,8 +283,9 @@ ZERO_API zero_status zero_reshard(zero_plan_t src_plan, zero_plan_t dst_plan, in
  * The fused step reads about ten bytes of gradient for each byte it writes.
  * With a write window, a wave whose results are ready holds its stores until
  * the GPU's constant-rate real-time counter is within the first open_ticks of
- * a period_ticks-long period, so the device's writes reach HBM in bursts
- * rather than as a thin stream between the reads.  A tick is one count of
+ * a period_ticks-long period, and a wave about to issue its first gradient
+ * loads waits until that opening has passed, so the device's writes reach HBM
+ * in bursts rather than as a thin stream between the reads.  A tick is one count of
  * that counter at the rate the device reports as hipDeviceAttributeWallClockRate
  * (100 MHz on MI355X: 10 ns).
  *   period_ticks  -1: automatic (the default): the library picks the window
