@@ -148,7 +148,7 @@ __device__ __forceinline__ void await_write_window(uint32_t period, uint32_t ope
 // (9% and 3% written) unchanged.  Gating every rank batch as well helped
 // N_d = 16 a little more but cost N_d = 24 and 32 up to 3%.
 __device__ __forceinline__ void await_read_window(uint32_t period, uint32_t open) {
-  if (period == 0) return;
+  if (period == 0 || open >= period) return;   // no window, or no closed phase to load in
   const uint64_t now = __builtin_amdgcn_s_memrealtime();
   const uint64_t phase = now % period;
   if (phase >= open) return;
