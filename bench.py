@@ -23,6 +23,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 7.5B-stag
 """
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -34,6 +35,8 @@ sys.path.insert(0, ROOT)
 METRIC = "fused ZeRO shard-step params/s + HBM GB/s (% of peak), 7.5B at N_d=64"
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "zero_sharded_mixed_02_amd", "csrc", "zero_kernels.hip")
+# The kernels' own source and the header of constants and argument layouts they are built from.
+KERNEL_SOURCES = (KERNEL_SRC, os.path.join(ROOT, "zero_sharded_mixed_02_amd", "csrc", "zero_internal.h"))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_step_7p5B_nd64_traffic.json")
 
 DTYPE_NAME = {0: "fp32", 1: "fp16", 2: "bf16"}
@@ -43,9 +46,25 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def code_text(path: str) -> str:
+    """A C++ source's text with its comments removed and every run of
+    whitespace made one space: what the compiler sees, up to layout.  (The
+    kernel sources hold no string literal with a comment marker in it.)"""
+    with open(path) as f:
+        t = f.read()
+    t = re.sub(r"/\*.*?\*/", " ", t, flags=re.S)
+    t = re.sub(r"//[^\n]*", " ", t)
+    return " ".join(t.split())
+
+
 def kernel_source_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernels' code (comments and layout excluded, so that editing
+    a comment keeps a counter record valid)."""
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(code_text(p).encode())
+        h.update(b"\0")
+    return h.hexdigest()[:16]
 
 
 def algorithmic_bytes_per_param(n_d: int, gdt_bytes: int = 2, pdt_bytes: int = 2) -> int:

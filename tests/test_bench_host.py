@@ -35,6 +35,34 @@ def test_traffic_only_for_its_kernel_source(tmp_path, monkeypatch):
     assert bench.measured_traffic(154.0) is None
 
 
+def test_kernel_hash_ignores_comments_not_code(tmp_path, monkeypatch):
+    srcs = []
+    for i, p in enumerate(bench.KERNEL_SOURCES):
+        q = tmp_path / f"src{i}"
+        q.write_text(open(p).read())
+        srcs.append(q)
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", tuple(str(q) for q in srcs))
+    base = bench.kernel_source_sha()
+    assert base == bench.kernel_source_sha()
+    text = srcs[0].read_text()
+    srcs[0].write_text("// a new comment\n" + text.replace("\n", "  /* a block\n comment */\n", 1) + "\n\n")
+    assert bench.kernel_source_sha() == base
+    srcs[0].write_text(text.replace("kTile = 512", "kTile = 256", 1))
+    assert "kTile = 512" in text and bench.kernel_source_sha() != base
+    srcs[0].write_text(text)
+    srcs[1].write_text(srcs[1].read_text() + "\nconstexpr int kExtra = 1;\n")
+    assert bench.kernel_source_sha() != base
+
+
+def test_kernel_sources_hold_no_comment_marker_in_a_string():
+    # code_text strips comments with two regular expressions, which would
+    # misread a string literal holding "//" or "/*".
+    import re
+    for p in bench.KERNEL_SOURCES:
+        for lit in re.findall(r'"(?:[^"\\\n]|\\.)*"', open(p).read()):
+            assert "//" not in lit and "/*" not in lit, (p, lit)
+
+
 def _counters(path, rows):
     with open(path, "w", newline="") as fh:
         w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])

@@ -144,9 +144,10 @@ __device__ __forceinline__ void await_write_window(uint32_t period, uint32_t ope
 // newly started waves do not mix with them.  Waves already loading are not
 // held (only the first load of a wave is gated).  Measured on MI355X against
 // the store window alone: the 13B step (N_d = 16, 24% of its bytes written)
-// 1.5% faster, N_d = 24 and 32 0.6-1.2%, the 7.5B step and the reduction
-// (9% and 3% written) unchanged.  Gating every rank batch as well helped
-// N_d = 16 a little more but cost N_d = 24 and 32 up to 3%.
+// 1.5% faster, N_d = 24 and 32 0.6-1.2%; the 7.5B step (9% written) about 1%
+// faster in fresh processes and unchanged late in a long one; the reduction
+// (3% written) unchanged.  Gating every rank batch as well helped N_d = 16 a
+// little more but cost N_d = 24 and 32 up to 3%.
 __device__ __forceinline__ void await_read_window(uint32_t period, uint32_t open) {
   if (period == 0 || open >= period) return;   // no window, or no closed phase to load in
   const uint64_t now = __builtin_amdgcn_s_memrealtime();
