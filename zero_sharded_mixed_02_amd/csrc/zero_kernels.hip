@@ -614,7 +614,8 @@ __global__ void __launch_bounds__(kThreads) copy_kernel(const CopyArgs a) {
 // among the step's reads; and the step then finds this part of its state in
 // that cache.  After gradients written with ordinary stores the step is ~11%
 // faster (7.5B, N_d = 64); after a step, or gradients written non-temporally,
-// the read repays its own time.  Full workgroups take every unit without
+// the step gains less than the read takes (1-2% net cost), which is why the
+// read is opt-in.  Full workgroups take every unit without
 // per-unit checks (wave w reads the workgroup's w-th 64 x kWarmUnits units
 // as 1 KiB spans); the last workgroup of a range checks each unit.
 __global__ void __launch_bounds__(kWarmThreads) warm_kernel(const WarmArgs a) {
