@@ -970,6 +970,89 @@ def measure_slice_placement(torch, rounds=3):
     return out
 
 
+REALLOC_ALLOCATIONS = 4
+REALLOC_ROUNDS = 2
+REALLOC_CASES = (("fused", "auto"), ("fused", "off"), ("reduce", "auto"), ("reduce", "off"))
+
+
+def reallocation_run(torch, allocations=REALLOC_ALLOCATIONS, rounds=REALLOC_ROUNDS):
+    """The fused 7.5B step and the reduction on the process's first
+    allocation of the workload's buffers, then after the buffers were freed
+    (with the allocator's cache emptied) and allocated again, allocations - 1
+    times.  The caching allocator hands back the same virtual addresses; the
+    driver backs them with physical memory of its own choosing, and which HBM
+    channel and bank a byte lands on follows its physical address.  Each
+    allocation times every case of REALLOC_CASES (automatic write window, or
+    none) as a block of launches back to back (3 warm-up calls, one untimed,
+    20 timed), `rounds` times in that order; the best of the rounds is
+    reported.  Prints one JSON line.  Meant to be the first thing a fresh
+    process does."""
+    import zero_sharded_mixed_02_amd as Z
+    from synth.workloads import WORKLOADS, GpuRun
+    torch.cuda.init()
+    t = [0]
+    out = []
+    first = None
+    for i in range(allocations):
+        run = GpuRun(WORKLOADS["7.5B-stage2"])
+        S, L0 = run.S, run.layers[0]
+        red = torch.empty(S, dtype=torch.float32, device="cuda")
+        ptrs = [L0["compact_rows"].data_ptr(), L0["master"].data_ptr(), L0["m"].data_ptr(), L0["v"].data_ptr(),
+                run.full.data_ptr(), red.data_ptr()]
+        first = ptrs if first is None else first
+        run.fill_grads(1)
+
+        def fused():
+            t[0] += 1
+            run.step(t[0])
+
+        fns = {"fused": fused, "reduce": lambda: run.reduce(red)}
+        times = {}
+        try:
+            for _ in range(rounds):
+                for name, win in REALLOC_CASES:
+                    Z.zero_set_write_window(-1 if win == "auto" else 0)
+                    times.setdefault(f"{name}_{win}", []).append(_time_launches(torch, fns[name]))
+        finally:
+            Z.zero_set_write_window(-1)
+        names = ("grad_rows", "master", "m", "v", "params", "reduced")
+        rec = {"allocation": i, "same_virtual_addresses_as_first": ptrs == first,
+               "addresses": {n: hex(p) for n, p in zip(names, ptrs)},
+               "mib_from_first": {n: (p - f) / 2**20 for n, p, f in zip(names, ptrs, first)}}
+        for k, v in times.items():
+            nbytes = (algorithmic_bytes_per_param(64) if k.startswith("fused") else 2 * 64 + 4) * S
+            rec[k] = {"ms": round(min(v), 4), "frac": round(nbytes / (min(v) / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        out.append(rec)
+        log(f"allocation {i}: " + "  ".join(f"{k} {rec[k]['ms']:.4f}" for k in times))
+        del run, red, fns, fused
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    print(json.dumps({"workload": "7.5B-stage2", "reallocation": out}), flush=True)
+
+
+def reallocation_counters(csv_path, allocations=REALLOC_ALLOCATIONS, rounds=REALLOC_ROUNDS):
+    """Median per allocation of each counter in a rocprofv3 --pmc CSV of
+    `bench.py --reallocation`, over the fused step's launches with the
+    automatic window (the dispatches of step_vec_kernel<0, 2, 1, 64> in
+    order: per allocation and round, 24 with the window, then 24 without)."""
+    import csv
+    import statistics
+    per = {}
+    with open(csv_path, newline="") as fh:
+        for r in csv.DictReader(fh):
+            if "step_vec_kernel<0, 2, 1, 64>" in r["Kernel_Name"]:
+                per.setdefault(int(r["Dispatch_Id"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    ds = [per[d] for d in sorted(per)]
+    block = 24
+    if len(ds) != allocations * rounds * 2 * block:
+        raise SystemExit(f"expected {allocations * rounds * 2 * block} fused dispatches, found {len(ds)}")
+    out = []
+    for a in range(allocations):
+        sel = [ds[(a * rounds + r) * 2 * block + k] for r in range(rounds) for k in range(block)]
+        out.append({c: statistics.median(x[c] for x in sel) for c in sorted(sel[0])})
+    print(json.dumps({"fused_auto_window_median_per_allocation": out}, indent=1))
+
+
 def measure_stage3_overlap(torch, splits=(16, 32, 64)):
     """The Stage-3 8-layer loop with a layer-compute stand-in: serial,
     prefetching on a second stream, and prefetching with the CUs split."""
@@ -1245,6 +1328,11 @@ def main():
                     help="also time the step after each predecessor of FILL_ORDER_VARIANTS (adds 'fill_order')")
     ap.add_argument("--fill-order-run", nargs="+", metavar="VARIANT",
                     help="run (predecessor, step) pairs of the given variants for rocprofv3 --pmc runs and exit")
+    ap.add_argument("--reallocation", action="store_true",
+                    help="time the fused 7.5B step and the reduction on a first allocation and on the same "
+                         "buffers freed and allocated again, print one JSON line and exit")
+    ap.add_argument("--reallocation-counters", metavar="CSV",
+                    help="medians per allocation of a rocprofv3 --pmc CSV of --reallocation, and exit")
     ap.add_argument("--counter-run", action="store_true",
                     help="run each entry point on its workload twice for rocprofv3 --pmc runs and exit")
     ap.add_argument("--write-counter-table", nargs=6,
@@ -1275,6 +1363,9 @@ def main():
     if args.write_counter_table:
         write_counter_table(*args.write_counter_table)
         return
+    if args.reallocation_counters:
+        reallocation_counters(args.reallocation_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the step is one rank's share, and its "
               "throughput at N GPUs is N times the one-GPU figure with no collective in the path; "
@@ -1291,6 +1382,11 @@ def main():
         from __graft_entry__ import _ensure_built
         _ensure_built()
         counter_run(torch)
+        return
+    if args.reallocation:
+        from __graft_entry__ import _ensure_built
+        _ensure_built()
+        reallocation_run(torch)
         return
     if args.copy_probe:
         copy_probe(torch)
