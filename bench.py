@@ -204,6 +204,27 @@ def _frac(e):
     return {"ms": round(e["ms"], 4), "gbps": round(e["gbps"], 1), "frac": round(e["frac_hbm_peak"], 4)}
 
 
+# Releasing device memory has a cost that shows up afterwards: for about a
+# second per ~30 GB released, kernels that stream HBM run a few percent slower
+# (the fused 7.5B step 2.83 ms instead of 2.71), with the same buffers, and not
+# when nothing was released; consistent with the driver clearing the released
+# memory in the background.  Measurements that follow a release wait it out.
+SETTLE_BYTES_PER_S = 16e9
+SETTLE_MAX_S = 10.0
+
+
+def release(torch):
+    """Free what torch's caching allocator holds, then wait in proportion to
+    the bytes it gave back, so that the next measurement does not run beside
+    the aftermath of the release."""
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_reserved()
+    torch.cuda.empty_cache()
+    freed = before - torch.cuda.memory_reserved()
+    if freed > 0:
+        time.sleep(min(SETTLE_MAX_S, 0.2 + freed / SETTLE_BYTES_PER_S))
+
+
 def measure_kernels_compact(torch):
     """Every entry point at its own workload, each as (ms, GB/s, share of
     peak) from HIP events on the launch stream: the unfused pair on the 7.5B
@@ -221,8 +242,7 @@ def measure_kernels_compact(torch):
     t = [0]
 
     def free():
-        torch.cuda.synchronize()
-        torch.cuda.empty_cache()
+        release(torch)
 
     def fused_of(run, layer=None):
         def f():
@@ -311,8 +331,7 @@ def measure_calibration(torch):
     res["runtime_copy"] = _frac(e)
     res["runtime_copy"]["bytes_per_launch"] = 2 * CAL_BYTES
     del src, dst, sink
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
+    release(torch)
     log("calibration done: " + ", ".join(f"{k} {v['gbps']:.0f} GB/s" for k, v in res.items()))
     return res
 
@@ -501,8 +520,7 @@ def measure_fill_order(torch, reps=6):
                         "frac": round(nbytes / (med / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
         log(f"fill order {variant}: {med:.3f} ms")
     del run, spare
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
+    release(torch)
     return out
 
 
@@ -543,8 +561,7 @@ def measure_kernels(torch):
     out = {}
 
     def free():
-        torch.cuda.synchronize()
-        torch.cuda.empty_cache()
+        release(torch)
 
     # 7.5B, N_d = 64: fused, and the two unfused halves.
     cfg = WORKLOADS["7.5B-stage2"]
@@ -754,8 +771,7 @@ def measure_windows(torch):
             sweep("reduce_7.5B_nd64", lambda: run.reduce(red), (2 * n_d + 4) * S, S, reps)
             del red
         del run
-        torch.cuda.synchronize()
-        torch.cuda.empty_cache()
+        release(torch)
     return out
 
 
@@ -910,8 +926,7 @@ def measure_window_shapes(torch, rounds=3):
         out[key] = {"frac_hbm_peak": frac, "best": best, "auto_over_best": round(frac["auto"] / frac[best], 4)}
         log(f"window shape {key}: off {frac['off']:.3f}, auto {frac['auto']:.3f}, best {best} {frac[best]:.3f}")
         del g, master, m, v, full, src, plan
-        torch.cuda.synchronize()
-        torch.cuda.empty_cache()
+        release(torch)
     return out
 
 
@@ -965,92 +980,79 @@ def measure_slice_placement(torch, rounds=3):
         out[name] = {"stride_bytes": strides[name], "ms": ms, "frac": 154 * S / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS}
         log(f"slice placement {name}: stride {strides[name]} B, {ms:.4f} ms, frac {out[name]['frac']:.4f}")
     del pool, run
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
+    release(torch)
     return out
 
 
-REALLOC_ALLOCATIONS = 4
-REALLOC_ROUNDS = 2
-REALLOC_CASES = (("fused", "auto"), ("fused", "off"), ("reduce", "auto"), ("reduce", "off"))
-
-
-def reallocation_run(torch, allocations=REALLOC_ALLOCATIONS, rounds=REALLOC_ROUNDS):
-    """The fused 7.5B step and the reduction on the process's first
-    allocation of the workload's buffers, then after the buffers were freed
-    (with the allocator's cache emptied) and allocated again, allocations - 1
-    times.  The caching allocator hands back the same virtual addresses; the
-    driver backs them with physical memory of its own choosing, and which HBM
-    channel and bank a byte lands on follows its physical address.  Each
-    allocation times every case of REALLOC_CASES (automatic write window, or
-    none) as a block of launches back to back (3 warm-up calls, one untimed,
-    20 timed), `rounds` times in that order; the best of the rounds is
-    reported.  Prints one JSON line.  Meant to be the first thing a fresh
-    process does."""
+def reallocation_run(torch, rounds=8):
+    """What a release of device memory does to the measurements after it.
+    The fused 7.5B step (automatic write window) and the reduction (no
+    window), each a block of 20 launches back to back, round after round with
+    the time since the start: on the process's first allocation of the
+    workload; on a second allocation made right after the first was freed
+    (torch's cache emptied, no wait); on a third made after freeing and
+    waiting 3 s; and on a fourth made while the third is still held, so that
+    nothing was freed just before it.  Prints one JSON line."""
     import zero_sharded_mixed_02_amd as Z
     from synth.workloads import WORKLOADS, GpuRun
     torch.cuda.init()
     t = [0]
-    out = []
-    first = None
-    for i in range(allocations):
-        run = GpuRun(WORKLOADS["7.5B-stage2"])
-        S, L0 = run.S, run.layers[0]
-        red = torch.empty(S, dtype=torch.float32, device="cuda")
-        ptrs = [L0["compact_rows"].data_ptr(), L0["master"].data_ptr(), L0["m"].data_ptr(), L0["v"].data_ptr(),
-                run.full.data_ptr(), red.data_ptr()]
-        first = ptrs if first is None else first
-        run.fill_grads(1)
+    t0 = time.perf_counter()
 
+    def alloc():
+        run = GpuRun(WORKLOADS["7.5B-stage2"])
+        red = torch.empty(run.S, dtype=torch.float32, device="cuda")
+        run.fill_grads(1)
+        torch.cuda.synchronize()
+        return run, red
+
+    def series(run, red):
         def fused():
             t[0] += 1
             run.step(t[0])
-
-        fns = {"fused": fused, "reduce": lambda: run.reduce(red)}
-        times = {}
+        S, out = run.S, []
         try:
             for _ in range(rounds):
-                for name, win in REALLOC_CASES:
-                    Z.zero_set_write_window(-1 if win == "auto" else 0)
-                    times.setdefault(f"{name}_{win}", []).append(_time_launches(torch, fns[name]))
+                Z.zero_set_write_window(-1)
+                f = _time_launches(torch, fused)
+                Z.zero_set_write_window(0)
+                r = _time_launches(torch, lambda: run.reduce(red))
+                Z.zero_set_write_window(-1)
+                out.append({"t_s": round(time.perf_counter() - t0, 3), "fused_window_ms": round(f, 4),
+                            "fused_frac": round(algorithmic_bytes_per_param(64) * S / (f / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+                            "reduce_no_window_ms": round(r, 4)})
         finally:
             Z.zero_set_write_window(-1)
-        names = ("grad_rows", "master", "m", "v", "params", "reduced")
-        rec = {"allocation": i, "same_virtual_addresses_as_first": ptrs == first,
-               "addresses": {n: hex(p) for n, p in zip(names, ptrs)},
-               "mib_from_first": {n: (p - f) / 2**20 for n, p, f in zip(names, ptrs, first)}}
-        for k, v in times.items():
-            nbytes = (algorithmic_bytes_per_param(64) if k.startswith("fused") else 2 * 64 + 4) * S
-            rec[k] = {"ms": round(min(v), 4), "frac": round(nbytes / (min(v) / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
-        out.append(rec)
-        log(f"allocation {i}: " + "  ".join(f"{k} {rec[k]['ms']:.4f}" for k in times))
-        del run, red, fns, fused
+        return out
+
+    def freed_gb():
         torch.cuda.synchronize()
+        before = torch.cuda.memory_reserved()
         torch.cuda.empty_cache()
-    print(json.dumps({"workload": "7.5B-stage2", "reallocation": out}), flush=True)
+        return round((before - torch.cuda.memory_reserved()) / 1e9, 2)
 
+    def freed():
+        return freed_gb(), round(time.perf_counter() - t0, 3)
 
-def reallocation_counters(csv_path, allocations=REALLOC_ALLOCATIONS, rounds=REALLOC_ROUNDS):
-    """Median per allocation of each counter in a rocprofv3 --pmc CSV of
-    `bench.py --reallocation`, over the fused step's launches with the
-    automatic window (the dispatches of step_vec_kernel<0, 2, 1, 64> in
-    order: per allocation and round, 24 with the window, then 24 without)."""
-    import csv
-    import statistics
-    per = {}
-    with open(csv_path, newline="") as fh:
-        for r in csv.DictReader(fh):
-            if "step_vec_kernel<0, 2, 1, 64>" in r["Kernel_Name"]:
-                per.setdefault(int(r["Dispatch_Id"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
-    ds = [per[d] for d in sorted(per)]
-    block = 24
-    if len(ds) != allocations * rounds * 2 * block:
-        raise SystemExit(f"expected {allocations * rounds * 2 * block} fused dispatches, found {len(ds)}")
-    out = []
-    for a in range(allocations):
-        sel = [ds[(a * rounds + r) * 2 * block + k] for r in range(rounds) for k in range(block)]
-        out.append({c: statistics.median(x[c] for x in sel) for c in sorted(sel[0])})
-    print(json.dumps({"fused_auto_window_median_per_allocation": out}, indent=1))
+    res = {}
+    run, red = alloc()
+    res["first_allocation"] = {"rounds": series(run, red)}
+    del run, red
+    gb, at = freed()
+    run, red = alloc()
+    res["reallocated_at_once"] = {"freed_gb": gb, "released_at_s": at, "rounds": series(run, red)}
+    del run, red
+    gb, at = freed()
+    time.sleep(3.0)
+    run, red = alloc()
+    res["reallocated_after_3s"] = {"freed_gb": gb, "released_at_s": at, "rounds": series(run, red)}
+    run2, red2 = alloc()
+    res["second_set_nothing_freed"] = {"rounds": series(run2, red2)}
+    del run2, red2, run, red
+    release(torch)
+    for k, v in res.items():
+        log(f"{k}: " + " ".join(f"{x['fused_window_ms']:.3f}" for x in v["rounds"]))
+    print(json.dumps({"workload": "7.5B-stage2", "reallocation": res}), flush=True)
 
 
 def measure_stage3_overlap(torch, splits=(16, 32, 64)):
@@ -1066,8 +1068,7 @@ def measure_stage3_overlap(torch, splits=(16, 32, 64)):
     res["elastic_compute"] = _stage3_elastic(torch, run, t, res["gather_only_ms"] / run.cfg.layers)
     res["contention"] = _stage3_contention(torch, run, stage3_gemm_compute(torch, run))
     del run
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
+    release(torch)
     return res
 
 
@@ -1329,10 +1330,8 @@ def main():
     ap.add_argument("--fill-order-run", nargs="+", metavar="VARIANT",
                     help="run (predecessor, step) pairs of the given variants for rocprofv3 --pmc runs and exit")
     ap.add_argument("--reallocation", action="store_true",
-                    help="time the fused 7.5B step and the reduction on a first allocation and on the same "
-                         "buffers freed and allocated again, print one JSON line and exit")
-    ap.add_argument("--reallocation-counters", metavar="CSV",
-                    help="medians per allocation of a rocprofv3 --pmc CSV of --reallocation, and exit")
+                    help="time the fused 7.5B step and the reduction round by round on a first allocation, "
+                         "right after a release of device memory, and after waiting; print one JSON line and exit")
     ap.add_argument("--counter-run", action="store_true",
                     help="run each entry point on its workload twice for rocprofv3 --pmc runs and exit")
     ap.add_argument("--write-counter-table", nargs=6,
@@ -1362,9 +1361,6 @@ def main():
         return
     if args.write_counter_table:
         write_counter_table(*args.write_counter_table)
-        return
-    if args.reallocation_counters:
-        reallocation_counters(args.reallocation_counters)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the step is one rank's share, and its "
@@ -1540,8 +1536,7 @@ def main():
                     "step"},
     }
     del run
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
+    release(torch)
     if args.window is not None:   # the other measurements use the library's automatic choice
         import zero_sharded_mixed_02_amd as Z
         Z.zero_set_write_window(-1)

@@ -101,33 +101,30 @@ def test_refuses_more_than_one_gpu():
     assert "one GPU" in r.stderr or "--gpus 1" in r.stderr
 
 
-def test_reallocation_counters_take_the_windowed_launches(tmp_path, capsys):
-    # Per allocation and round: 24 windowed launches of the fused kernel, 24
-    # without a window, and reduce launches in between (another kernel).
-    fused = "void zk::(anonymous namespace)::step_vec_kernel<0, 2, 1, 64>(zk::StepArgs)"
-    other = "void zk::(anonymous namespace)::step_vec_kernel<2, 2, 1, 64>(zk::StepArgs)"
-    rows, d = [], 0
-    for a in range(bench.REALLOC_ALLOCATIONS):
-        for r in range(bench.REALLOC_ROUNDS):
-            for win in ("auto", "off"):
-                for k in range(24):
-                    d += 1
-                    v = 1000 * a + (5 if k == 0 else 1) if win == "auto" else -1
-                    rows.append((d, fused, "C", v))
-            for k in range(48):
-                d += 1
-                rows.append((d, other, "C", -7))
-    p = tmp_path / "c.csv"
-    with open(p, "w", newline="") as fh:
-        w = csv.writer(fh)
-        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
-        w.writerows(rows)
-    bench.reallocation_counters(str(p))
-    out = json.loads(capsys.readouterr().out)["fused_auto_window_median_per_allocation"]
-    assert [o["C"] for o in out] == [1000 * a + 1 for a in range(bench.REALLOC_ALLOCATIONS)]
-    with open(p, "w", newline="") as fh:
-        w = csv.writer(fh)
-        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
-        w.writerows(rows[:-60])
-    with pytest.raises(SystemExit):
-        bench.reallocation_counters(str(p))
+def test_release_waits_in_proportion_to_the_bytes_freed(monkeypatch):
+    class Cuda:
+        def __init__(self, before, after):
+            self.reserved = [before, after]
+            self.emptied = 0
+
+        def synchronize(self):
+            pass
+
+        def memory_reserved(self):
+            return self.reserved[self.emptied]
+
+        def empty_cache(self):
+            self.emptied = 1
+
+    class Torch:
+        def __init__(self, before, after):
+            self.cuda = Cuda(before, after)
+
+    slept = []
+    monkeypatch.setattr(bench.time, "sleep", slept.append)
+    bench.release(Torch(40e9, 8e9))          # 32 GB given back
+    assert slept == [pytest.approx(0.2 + 32e9 / bench.SETTLE_BYTES_PER_S)]
+    bench.release(Torch(8e9, 8e9))           # nothing given back: no wait
+    assert len(slept) == 1
+    bench.release(Torch(500e9, 0))           # capped
+    assert slept[-1] == bench.SETTLE_MAX_S
