@@ -222,11 +222,11 @@ ZERO_API zero_status zero_shard_reduce(zero_plan_t plan, int32_t rank, const zer
  * With slices, the kernel may hold its stores for a device-wide write window
  * (zero_set_write_window); the results never depend on it.
  * Performance: slices written just before the step with ordinary cached
- * stores slow it by about 12% on MI355X; written with non-temporal stores
+ * stores slow it by 15-17% on MI355X; written with non-temporal stores
  * (as zero_shard_reduce, zero_flatten and zero_gather_pack write their
  * outputs) they cost nothing.  A producer of the slices should store them
  * non-temporally; where it cannot, zero_set_warm_read(1) recovers most of
- * the loss (3.24 -> 2.91 ms for 7.5B at N_d = 64).  Where the slices sit
+ * the loss (3.14-3.22 -> 2.79-2.89 ms for 7.5B at N_d = 64).  Where the slices sit
  * matters too: every wave reads the
  * same offset of all n_d slices at once, and slices a power of two apart
  * (say 256 MiB) put those reads on the same HBM channels, which costs the
@@ -323,7 +323,7 @@ ZERO_API zero_status zero_set_write_window(int64_t period_ticks, int64_t open_ti
  * Infinity Cache keeps the last lines written with ordinary stores dirty;
  * when the gradient slices were just written that way (as a collective or a
  * backward kernel may write them), their write-backs otherwise fall among the
- * step's reads and cost it ~12% (7.5B, N_d = 64).  The warm-up read moves them
+ * step's reads and cost it 15-17% (7.5B, N_d = 64).  The warm-up read moves them
  * before the step: measured, the step is then ~11% faster (7.5% for a Stage-3
  * layer, 3% for 13B at N_d = 16), and the reduction ~11%.  When the slices are
  * already clean (written non-temporally, as zero_shard_reduce and the copies
