@@ -42,4 +42,11 @@ def gpu(zero_lib):
         pytest.skip("no GPU visible")
     from synth import _build
     _ensure(_build)
-    return torch.device("cuda:0")
+    yield torch.device("cuda:0")
+    # At the end of the session, hand the memory torch's allocator still holds
+    # back to the driver and wait until the memory system has absorbed the
+    # release (kernels that stream HBM run a few percent slower for about a
+    # second per ~30 GB released), so that whatever runs on the GPU next does
+    # not start inside that aftermath.
+    import bench
+    bench.release(torch)
