@@ -204,6 +204,12 @@ def _frac(e):
     return {"ms": round(e["ms"], 4), "gbps": round(e["gbps"], 1), "frac": round(e["frac_hbm_peak"], 4)}
 
 
+def _kentry(e):
+    """An entry point's compact record: _frac plus the parameters it handles
+    per second (shard elements updated, or layer / tensor elements moved)."""
+    return {**_frac(e), "params_per_s": round(e["elements_per_s"])}
+
+
 # Releasing device memory has a cost that shows up afterwards: for about a
 # second per ~30 GB released, kernels that stream HBM run a few percent slower
 # (the fused 7.5B step 2.83 ms instead of 2.71), with the same buffers, and not
@@ -254,25 +260,25 @@ def measure_kernels_compact(torch):
     S = run.S
     run.fill_grads(1)
     red = torch.empty(S, dtype=torch.float32, device="cuda")
-    out["reduce_7.5B_nd64"] = _frac(_entry(_time_launches(torch, lambda: run.reduce(red)), (2 * 64 + 4) * S, S))
+    out["reduce_7.5B_nd64"] = _kentry(_entry(_time_launches(torch, lambda: run.reduce(red)), (2 * 64 + 4) * S, S))
 
     def from_reduced():
         t[0] += 1
         run.step_from_reduced(t[0], red)
-    out["adam_from_reduced_7.5B"] = _frac(_entry(_time_launches(torch, from_reduced), 30 * S, S))
+    out["adam_from_reduced_7.5B"] = _kentry(_entry(_time_launches(torch, from_reduced), 30 * S, S))
     del red, run
     free()
     run = GpuRun(replace(WORKLOADS["7.5B-stage2"], align=1))
     S = run.S
     run.fill_grads(1)
-    out["fused_7.5B_nd64_align1"] = _frac(_entry(_time_launches(torch, fused_of(run)), (2 * 64 + 26) * S, S))
+    out["fused_7.5B_nd64_align1"] = _kentry(_entry(_time_launches(torch, fused_of(run)), (2 * 64 + 26) * S, S))
     del run
     free()
     log("7.5B kernels done")
     run = GpuRun(WORKLOADS["13B-stage1"])
     S = run.S
     run.fill_grads(1)
-    out["fused_13B_stage1_nd16"] = _frac(_entry(_time_launches(torch, fused_of(run), reps=10), (2 * 16 + 26) * S, S))
+    out["fused_13B_stage1_nd16"] = _kentry(_entry(_time_launches(torch, fused_of(run), reps=10), (2 * 16 + 26) * S, S))
     del run
     free()
     log("13B kernel done")
@@ -280,9 +286,9 @@ def measure_kernels_compact(torch):
     S, P = run.S, run.P
     run.fill_grads(1, 0)
     shards = list(run.layers[0]["shards"])
-    out["gather_pack_h8192_nd64"] = _frac(_entry(
+    out["gather_pack_h8192_nd64"] = _kentry(_entry(
         _time_launches(torch, lambda: Z.zero_gather_pack(run.plan, shards, Z.ZERO_F16, run.full)), 4 * P, P))
-    out["stage3_layer_h8192_nd64"] = _frac(_entry(_time_launches(torch, fused_of(run, 0)),
+    out["stage3_layer_h8192_nd64"] = _kentry(_entry(_time_launches(torch, fused_of(run, 0)),
                                                   4 * P + (2 * 64 + 26) * S, P))
     del run, shards
     free()
@@ -290,7 +296,7 @@ def measure_kernels_compact(torch):
     run = GpuRun(WORKLOADS["gpt2-small"])
     S = run.S
     run.fill_grads(1)
-    out["fused_gpt2_nd8"] = _frac(_entry(_time_launches(torch, fused_of(run)), (2 * 8 + 26) * S, S))
+    out["fused_gpt2_nd8"] = _kentry(_entry(_time_launches(torch, fused_of(run)), (2 * 8 + 26) * S, S))
     sizes = gpt2_small_sizes()
     tens = [torch.empty(n, dtype=torch.int16, device="cuda") for n in sizes]
     stream = torch.cuda.current_stream().cuda_stream
@@ -298,7 +304,7 @@ def measure_kernels_compact(torch):
         SG.fill(x.data_ptr(), synth.BF16, x.numel(), synth.key_of(2, 9, i, 0), 0, 1e-3, stream)
     flat = torch.empty(run.P, dtype=torch.int16, device="cuda")
     psi = sum(sizes)
-    out["flatten_gpt2_bf16"] = _frac(_entry(
+    out["flatten_gpt2_bf16"] = _kentry(_entry(
         _time_launches(torch, lambda: Z.zero_flatten(run.plan, tens, Z.ZERO_BF16, flat)), 4 * psi + 2 * (run.P - psi), psi))
     del run, tens, flat
     free()
