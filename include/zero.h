@@ -222,16 +222,18 @@ ZERO_API zero_status zero_shard_reduce(zero_plan_t plan, int32_t rank, const zer
  * With slices, the kernel may hold its stores for a device-wide write window
  * (zero_set_write_window); the results never depend on it.
  * Performance: slices written just before the step with ordinary cached
- * stores slow it by 15-17% on MI355X; written with non-temporal stores
- * (as zero_shard_reduce, zero_flatten and zero_gather_pack write their
- * outputs) they cost nothing.  A producer of the slices should store them
+ * stores slow it by 15-17% on MI355X; written with non-temporal stores (as
+ * zero_shard_reduce, zero_flatten and zero_gather_pack write their outputs)
+ * they cost nothing.  A producer of the slices should store them
  * non-temporally; where it cannot, zero_set_warm_read(1) recovers most of
- * the loss (3.14-3.22 -> 2.79-2.89 ms for 7.5B at N_d = 64).  Where the slices sit
- * matters too: every wave reads the
- * same offset of all n_d slices at once, and slices a power of two apart
- * (say 256 MiB) put those reads on the same HBM channels, which costs the
- * step 4-6%; staggering them by 1-4 KiB, or packing them back to back,
- * avoids it.
+ * the loss (3.14-3.22 -> 2.79-2.89 ms for 7.5B at N_d = 64).  Where the
+ * slices sit matters too: every wave reads the same offset of all n_d slices
+ * at once, and slices a power of two apart (say 256 MiB) put those reads on
+ * the same HBM channels, which costs the step 4-6%; staggering them by 1-4
+ * KiB, or packing them back to back, avoids it.  For about a second after a
+ * large release of device memory (about 1 s per 30 GB, e.g. an emptied
+ * allocator cache) the step runs 2-5% slower; keep its buffers allocated
+ * from step to step.
  * Errors: EINVAL for a bad rank, t < 1, nulls, misalignment, src->n != n_d,
  * overlapping outputs; EUNSUPPORTED for non-16-bit types or for the fused
  * path with n_d > ZERO_MAX_RANKS (use zero_shard_reduce, then reduced).
