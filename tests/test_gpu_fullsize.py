@@ -2,7 +2,8 @@
 benchmark times: the GPU runs the whole shard; the oracle computes a sample of
 its elements one by one (first and last 4096, every segment boundary, and
 random positions), which is exact because every operation of the step is
-elementwise in the shard index."""
+elementwise in the shard index.  For the benchmark's own workload the oracle
+also covers the whole shard (test_fused_7p5B_whole_shard)."""
 import numpy as np
 import pytest
 
@@ -62,6 +63,59 @@ def test_stage12_full_size(gpu, oracle_lib, name):
     got = run.fetch_at(J, ref.pos)
     r = assert_state(got, ref.state(), cfg.pdt, cfg.name)
     say(f"  sample of {J.size}: {r}")
+    _free(run)
+
+
+def _oracle_whole_shard(cfg, S: int, steps: int, n_chunks: int = 64):
+    """The oracle over the owner's whole shard: contiguous chunks of shard
+    indices, each an OracleRun on that sample, on a thread pool.  Every
+    operation of the step is elementwise in the shard index and the oracle's
+    C calls release the GIL, so the concatenated chunks are the whole-shard
+    result.  Returns (state dict over the whole shard, flat positions)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle.runner import OracleRun
+
+    def one(J):
+        ref = OracleRun(cfg, sample=J)
+        for t in range(1, steps + 1):
+            ref.fill_grads(t)
+            ref.step(t)
+            ref.layers[0]["slices"] = None
+        st = ref.state()
+        return {k: st[k] for k in ("master", "m", "v", "params")}, ref.pos
+
+    chunks = np.array_split(np.arange(S, dtype=np.int64), n_chunks)
+    with ThreadPoolExecutor(min(16, len(os.sched_getaffinity(0)))) as ex:
+        parts = list(ex.map(one, chunks))
+    state = {k: np.concatenate([p[0][k] for p in parts]) for k in ("master", "m", "v", "params")}
+    return state, np.concatenate([p[1] for p in parts])
+
+
+def test_fused_7p5B_whole_shard(gpu, oracle_lib):
+    """The benchmark's workload (7.5B, N_d = 64, owner 0), two steps, compared
+    over the WHOLE shard: every one of its 117,187,520 master, m, v and 16-bit
+    parameter values equals the oracle's bit for bit, and the 7.5e9-element
+    parameter buffer holds nothing but zeros outside the owner's range."""
+    import torch
+    from dataclasses import replace
+    cfg = replace(WORKLOADS["7.5B-stage2"], steps=2)
+    say(f"[whole shard] {cfg.name}: psi={cfg.psi} n_d={cfg.n_d} steps={cfg.steps}")
+    run = GpuRun(cfg)
+    S = run.S
+    for t in range(1, cfg.steps + 1):
+        run.fill_grads(t)
+        run.step(t)
+    torch.cuda.synchronize()
+    say(f"  GPU done, S={S}; oracle over the whole shard ...")
+    want, pos = _oracle_whole_shard(cfg, S, cfg.steps)
+    lo, hi = int(pos.min()), int(pos.max()) + 1
+    assert hi - lo == S, "owner 0 of a one-bucket plan owns one contiguous range"
+    outside = int(torch.count_nonzero(run.full[:lo]).item()) + int(torch.count_nonzero(run.full[hi:]).item())
+    assert outside == 0, f"{outside} parameter elements written outside the owner's range"
+    got = run.fetch_at(np.arange(S, dtype=np.int64), pos)
+    r = assert_state(got, want, cfg.pdt, cfg.name)
+    say(f"  whole shard of {S}: {r}")
     _free(run)
 
 
