@@ -177,6 +177,10 @@ bool encode_window(int64_t period_ticks, int64_t open_ticks, uint64_t& w) {
 // The kernel compiled for 16 ranks (a quarter of its bytes written) does best
 // at 0.74: 1.4-2.2% faster than at 0.62 on four shapes (13B, and 100M-400M
 // shards in bf16 and fp16), with the gain gone by 0.82 and a loss from 0.86.
+// Reduce-only launches (3-11% written) do best at 0.45: 0.2-4.6% faster than
+// at 0.62 on the 7.5B shard and N_d = 32, 128 and 200, in two same-process
+// comparisons; on the 16-rank kernel shorter periods lose (1.6% at 0.45), so
+// it keeps 0.62 there.
 // Launches with few ranks per written element or few elements gain nothing.
 // A launch of few generations does better with a shorter period: its waits at
 // the end are not hidden by later generations.  Up to 6 generations take at
@@ -197,7 +201,8 @@ constexpr double kAutoFullGenerations = 12.0;
 constexpr int64_t kAutoMinElems = int64_t(1) << 23;
 constexpr double kAutoStreamShare = 6.5e12 / 8.192e12;   // 6.5 TB/s on MI355X
 constexpr double kAutoPeriodShare = 0.62;                 // of one generation's streaming time
-constexpr double kAutoPeriodShare16 = 0.74;               //   for the 16-rank kernel
+constexpr double kAutoPeriodShare16 = 0.74;               //   for the 16-rank kernel's fused step
+constexpr double kAutoPeriodShareReduce = 0.45;           //   for other reduce-only launches
 constexpr double kAutoWideOpeningShare = 0.12;            // generic kernel: written share above which
 constexpr double kAutoWideOpening = 1.5;                  //   the opening is this multiple of it
 
@@ -212,7 +217,9 @@ void auto_window(int mode, int gdt, int pdt, int ndc, int n_ranks, int64_t elems
   const double read = 2.0 * n_ranks + (mode == zk::kFused ? 12.0 : (a.flags & zk::kFlagInitFromOut) ? 4.0 : 0.0);
   const double written = mode == zk::kFused ? 14.0 : 4.0;
   const double gen_bytes = (double)resident * zk::kStepThreads * zk::kStepVec * (read + written);
-  const double share = ndc == 16 ? kAutoPeriodShare16 : kAutoPeriodShare;
+  const bool fused = mode == zk::kFused;
+  const double share = ndc == 16 ? (fused ? kAutoPeriodShare16 : kAutoPeriodShare)
+                                 : (fused ? kAutoPeriodShare : kAutoPeriodShareReduce);
   double period = gen_bytes / (kAutoStreamShare * peak) * share * hz;
   const double gens = (double)blocks / resident;
   period *= gens < kAutoShortGenerations
